@@ -1,0 +1,353 @@
+"""ctypes binding of libfp8idx.so, the C ABI declared in include/fp8idx.h.
+
+Argument marshalling only: each function checks dtypes, devices and
+contiguity of torch tensors, takes their device pointers and the current
+HIP stream, calls the C entry point of the same name and raises
+``Fp8idxError`` on a non-OK status.  Output and workspace tensors the caller
+does not pass are allocated here with torch (device memory is the only thing
+torch provides); every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the library is not built, or the device
+is not a gfx950, the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8idx.so")
+
+H = 32
+D = 128
+
+STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "EDEVICE", 5: "EHIP"}
+MAP_NONE, MAP_TOKEN_TABLE, MAP_BLOCK_TABLE = 0, 1, 2
+OP_TOPK, OP_LOGITS_TOPK_RAGGED = 0, 1
+
+EXPORTED = (
+    "indexer_logits_ragged", "indexer_logits_paged", "indexer_topk",
+    "indexer_logits_topk_ragged", "indexer_logits_topk_paged",
+    "fp8idx_workspace_bytes", "fp8idx_workspace_bytes_paged", "fp8idx_rows_per_chunk",
+    "fp8idx_status_string", "fp8idx_last_hip_error", "fp8idx_version",
+)
+
+
+class Fp8idxError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+class _CMap(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("table", ctypes.c_void_p),
+        ("ld", ctypes.c_int64),
+        ("num_req", ctypes.c_int32),
+        ("cu_rows", ctypes.c_void_p),
+        ("rows_per_req", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+    ]
+
+
+_LIB = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfp8idx.so and declare its signatures (raises if it is missing)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built: run `python -m fp8_mqa_logits_amd.build` "
+            "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(path)
+    sig = {
+        "indexer_logits_ragged": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _I64, _I32, _P]),
+        "indexer_logits_paged": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I64,
+                                        _P, _I64, _I32, _I32, _P]),
+        "indexer_topk": (_I32, [_P, _I64, _I32, _I32, _P, _P, _I32, _I32, ctypes.POINTER(_CMap), _P, _I64,
+                                _P, _SZ, _P]),
+        "indexer_logits_topk_ragged": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                              ctypes.POINTER(_CMap), _P, _I64, _SZ, _P, _SZ, _P]),
+        "indexer_logits_topk_paged": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I64,
+                                             _I32, _I32, _I32, _P, _I64, _SZ, _P, _SZ, _P]),
+        "fp8idx_workspace_bytes": (_SZ, [_I32, _I32, _I64, _I32, _SZ]),
+        "fp8idx_workspace_bytes_paged": (_SZ, [_I32, _I32, _I32, _I32, _SZ]),
+        "fp8idx_rows_per_chunk": (_I32, [_SZ, _I64, _I32]),
+        "fp8idx_status_string": (ctypes.c_char_p, [_I32]),
+        "fp8idx_last_hip_error": (_I32, []),
+        "fp8idx_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = L
+    return L
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        L = load_library()
+        msg = L.fp8idx_status_string(status).decode()
+        if status == 5:
+            msg += f" (hipError {L.fp8idx_last_hip_error()})"
+        raise Fp8idxError(fn, status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device, stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(dev).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.device:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.device
+
+
+def _need(t: torch.Tensor, name: str, dtypes, dev: torch.device) -> torch.Tensor:
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _fp8(t: torch.Tensor, name: str, dev: torch.device) -> torch.Tensor:
+    _need(t, name, (torch.uint8, torch.float8_e4m3fn), dev)
+    return t.view(torch.uint8) if t.dtype != torch.uint8 else t
+
+
+_F32 = (torch.float32,)
+_I32T = (torch.int32,)
+
+
+@dataclasses.dataclass
+class TopkMap:
+    """Index map of the top-k stage (fp8idx_map): kind, table [num_req, ld] int32 and extras."""
+
+    kind: int = MAP_NONE
+    table: Optional[torch.Tensor] = None
+    cu_rows: Optional[torch.Tensor] = None
+    rows_per_req: int = 1
+    page_size: int = 1
+
+    def to_c(self) -> _CMap:
+        m = _CMap()
+        m.kind = self.kind
+        if self.table is not None:
+            if self.table.dtype != torch.int32 or not self.table.is_contiguous() or self.table.dim() != 2:
+                raise ValueError("map table must be a contiguous 2-D int32 tensor")
+            m.table = self.table.data_ptr()
+            m.ld = self.table.shape[1]
+            m.num_req = self.table.shape[0]
+        if self.cu_rows is not None:
+            if self.cu_rows.dtype != torch.int32 or not self.cu_rows.is_contiguous():
+                raise ValueError("cu_rows must be a contiguous int32 tensor")
+            m.cu_rows = self.cu_rows.data_ptr()
+        m.rows_per_req = self.rows_per_req
+        m.page_size = self.page_size
+        return m
+
+
+def _cmap(map_: Optional[TopkMap]):
+    if map_ is None:
+        return None
+    return ctypes.byref(map_.to_c())
+
+
+# ---------------------------------------------------------------------------
+# Pure host helpers
+# ---------------------------------------------------------------------------
+
+def fp8idx_workspace_bytes(op: int, rows: int, width: int, k: int, logits_cap_bytes: int = 0) -> int:
+    return int(load_library().fp8idx_workspace_bytes(op, rows, width, k, logits_cap_bytes))
+
+
+def fp8idx_workspace_bytes_paged(B: int, next_n: int, width: int, k: int, logits_cap_bytes: int = 0) -> int:
+    return int(load_library().fp8idx_workspace_bytes_paged(B, next_n, width, k, logits_cap_bytes))
+
+
+def fp8idx_rows_per_chunk(logits_cap_bytes: int, width: int, rows: int) -> int:
+    return int(load_library().fp8idx_rows_per_chunk(logits_cap_bytes, width, rows))
+
+
+def fp8idx_version() -> str:
+    return load_library().fp8idx_version().decode()
+
+
+def _workspace(nbytes: int, dev: torch.device, ws: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    if ws.dtype != torch.uint8 or ws.device != dev or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    off = (-ws.data_ptr()) % 256
+    avail = ws.numel() - off
+    return ws.data_ptr() + off, max(0, avail)
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def indexer_logits_ragged(q, kv, kv_scale, weights, ks, ke, *, clean: bool = True,
+                          logits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Ragged-prefill logits [m, n] float32 (or into ``logits`` [m, ld >= n])."""
+    dev = _dev(q, "q")
+    q8 = _fp8(q, "q", dev)
+    kv8 = _fp8(kv, "kv", dev)
+    m, n = q8.shape[0], kv8.shape[0]
+    if q8.shape[1:] != (H, D) or kv8.shape[1:] != (D,):
+        raise ValueError("q must be [m, 32, 128] and kv [n, 128]")
+    _need(kv_scale, "kv_scale", _F32, dev)
+    _need(weights, "weights", _F32, dev)
+    _need(ks, "ks", _I32T, dev)
+    _need(ke, "ke", _I32T, dev)
+    if logits is None:
+        logits = torch.empty((m, n), dtype=torch.float32, device=dev)
+    else:
+        _need(logits, "logits", _F32, dev)
+    with torch.cuda.device(dev):
+        st = load_library().indexer_logits_ragged(
+            _ptr(q8), _ptr(kv8), _ptr(kv_scale), _ptr(weights), _ptr(ks), _ptr(ke), m, n, H, D,
+            _ptr(logits), logits.shape[1] if logits.dim() == 2 else n, int(bool(clean)), _stream(dev, stream))
+    _check("indexer_logits_ragged", st)
+    return logits
+
+
+def indexer_logits_paged(q, kv_pool, scale_pool, weights, row_len, block_table, *, width: int,
+                         clean: bool = True, logits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Paged-decode logits [B * next_n, width] float32."""
+    dev = _dev(q, "q")
+    q8 = _fp8(q, "q", dev)
+    pool8 = _fp8(kv_pool, "kv_pool", dev)
+    if q8.dim() != 4 or q8.shape[2:] != (H, D):
+        raise ValueError("q must be [B, next_n, 32, 128]")
+    B, nn = q8.shape[0], q8.shape[1]
+    if pool8.dim() != 3 or pool8.shape[2] != D:
+        raise ValueError("kv_pool must be [pages, page_size, 128]")
+    _need(scale_pool, "scale_pool", _F32, dev)
+    _need(weights, "weights", _F32, dev)
+    _need(row_len, "row_len", _I32T, dev)
+    _need(block_table, "block_table", _I32T, dev)
+    if logits is None:
+        logits = torch.empty((B * nn, width), dtype=torch.float32, device=dev)
+    else:
+        _need(logits, "logits", _F32, dev)
+    with torch.cuda.device(dev):
+        st = load_library().indexer_logits_paged(
+            _ptr(q8), _ptr(pool8), _ptr(scale_pool), _ptr(weights), _ptr(row_len), _ptr(block_table),
+            B, nn, H, D, pool8.shape[1], block_table.shape[1], pool8.shape[0],
+            _ptr(logits), logits.shape[1], int(width), int(bool(clean)), _stream(dev, stream))
+    _check("indexer_logits_paged", st)
+    return logits
+
+
+def indexer_topk(logits, ke, k: int, *, ks=None, width: Optional[int] = None, row0: int = 0,
+                 map: Optional[TopkMap] = None, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Top-k [rows, k] int32 over logits [rows, ld] within [ks, ke)."""
+    dev = _dev(logits, "logits")
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be a 2-D float32 tensor with unit column stride")
+    rows, ld = logits.shape[0], logits.stride(0) if logits.shape[0] > 1 else logits.shape[1]
+    width = logits.shape[1] if width is None else int(width)
+    _need(ke, "ke", _I32T, dev)
+    if ks is not None:
+        _need(ks, "ks", _I32T, dev)
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=dev)
+    else:
+        _need(out, "out", _I32T, dev)
+    L = load_library()
+    need = int(L.fp8idx_workspace_bytes(OP_TOPK, rows, width, k, 0))
+    wp, wb = _workspace(need, dev, workspace)
+    with torch.cuda.device(dev):
+        st = L.indexer_topk(_ptr(logits), ld, rows, width, _ptr(ks), _ptr(ke), k, row0, _cmap(map),
+                            _ptr(out), out.shape[1], wp, wb, _stream(dev, stream))
+    _check("indexer_topk", st)
+    return out
+
+
+def indexer_logits_topk_ragged(q, kv, kv_scale, weights, ks, ke, k: int, *,
+                               map: Optional[TopkMap] = None, logits_cap_bytes: int = 0,
+                               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                               stream=None) -> torch.Tensor:
+    """Fused ragged logits + top-k, row-chunked under ``logits_cap_bytes`` (0 = one chunk)."""
+    dev = _dev(q, "q")
+    q8 = _fp8(q, "q", dev)
+    kv8 = _fp8(kv, "kv", dev)
+    m, n = q8.shape[0], kv8.shape[0]
+    if q8.shape[1:] != (H, D) or kv8.shape[1:] != (D,):
+        raise ValueError("q must be [m, 32, 128] and kv [n, 128]")
+    _need(kv_scale, "kv_scale", _F32, dev)
+    _need(weights, "weights", _F32, dev)
+    _need(ks, "ks", _I32T, dev)
+    _need(ke, "ke", _I32T, dev)
+    if out is None:
+        out = torch.empty((m, k), dtype=torch.int32, device=dev)
+    else:
+        _need(out, "out", _I32T, dev)
+    L = load_library()
+    need = int(L.fp8idx_workspace_bytes(OP_LOGITS_TOPK_RAGGED, m, n, k, logits_cap_bytes))
+    wp, wb = _workspace(need, dev, workspace)
+    with torch.cuda.device(dev):
+        st = L.indexer_logits_topk_ragged(
+            _ptr(q8), _ptr(kv8), _ptr(kv_scale), _ptr(weights), _ptr(ks), _ptr(ke), m, n, H, D, k,
+            _cmap(map), _ptr(out), out.shape[1], logits_cap_bytes, wp, wb, _stream(dev, stream))
+    _check("indexer_logits_topk_ragged", st)
+    return out
+
+
+def indexer_logits_topk_paged(q, kv_pool, scale_pool, weights, row_len, block_table, k: int, *,
+                              width: int, map_to_slots: bool = True, logits_cap_bytes: int = 0,
+                              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                              stream=None) -> torch.Tensor:
+    """Fused paged logits + top-k -> [B * next_n, k] int32 physical slots (or raw positions)."""
+    dev = _dev(q, "q")
+    q8 = _fp8(q, "q", dev)
+    pool8 = _fp8(kv_pool, "kv_pool", dev)
+    if q8.dim() != 4 or q8.shape[2:] != (H, D):
+        raise ValueError("q must be [B, next_n, 32, 128]")
+    B, nn = q8.shape[0], q8.shape[1]
+    _need(scale_pool, "scale_pool", _F32, dev)
+    _need(weights, "weights", _F32, dev)
+    _need(row_len, "row_len", _I32T, dev)
+    _need(block_table, "block_table", _I32T, dev)
+    if out is None:
+        out = torch.empty((B * nn, k), dtype=torch.int32, device=dev)
+    else:
+        _need(out, "out", _I32T, dev)
+    L = load_library()
+    need = int(L.fp8idx_workspace_bytes_paged(B, nn, width, k, logits_cap_bytes))
+    wp, wb = _workspace(need, dev, workspace)
+    with torch.cuda.device(dev):
+        st = L.indexer_logits_topk_paged(
+            _ptr(q8), _ptr(pool8), _ptr(scale_pool), _ptr(weights), _ptr(row_len), _ptr(block_table),
+            B, nn, H, D, pool8.shape[1], block_table.shape[1], pool8.shape[0], int(width), k,
+            int(bool(map_to_slots)), _ptr(out), out.shape[1], logits_cap_bytes, wp, wb, _stream(dev, stream))
+    _check("indexer_logits_topk_paged", st)
+    return out

@@ -1,0 +1,338 @@
+// C ABI of the fp8 MQA indexer library: argument validation, device checks,
+// workspace arithmetic and the row-chunked fused loop.  Every kernel launch
+// goes on the caller's stream; nothing here allocates or synchronises.
+
+#include <fp8idx.h>
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+#include <mutex>
+
+#include "launch.hpp"
+
+namespace {
+
+using fp8idx::DeviceInfo;
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+DeviceInfo g_dev_info[kMaxDevices];
+int g_dev_ok[kMaxDevices];
+
+fp8idx_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int32_t)e;
+  return FP8IDX_EHIP;
+}
+
+// Current device must be a gfx950; properties are read once per device.
+fp8idx_status current_device(DeviceInfo* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8IDX_EDEVICE;
+  std::call_once(g_dev_once[dev], [dev]() {
+    hipDeviceProp_t p;
+    std::memset(&p, 0, sizeof(p));
+    if (hipGetDeviceProperties(&p, dev) == hipSuccess) {
+      g_dev_ok[dev] = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+      g_dev_info[dev].cu_count = p.multiProcessorCount;
+    } else {
+      g_dev_ok[dev] = 0;
+    }
+  });
+  if (!g_dev_ok[dev]) return FP8IDX_EDEVICE;
+  *out = g_dev_info[dev];
+  return FP8IDX_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t align256(size_t x) { return (x + 255u) & ~(size_t)255u; }
+
+// Leading dimension of the float32 logits the fused entries keep in the
+// workspace: the key count rounded up to 4 floats (16-byte rows).
+int64_t ws_logits_ld(int64_t width) { return (width + 3) / 4 * 4; }
+
+int32_t rows_per_chunk(size_t cap, int64_t ld, int32_t rows) {
+  if (rows <= 0) return 0;
+  if (cap == 0) return rows;
+  const int64_t r = (int64_t)(cap / ((size_t)std::max<int64_t>(ld, 1) * 4u));
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(rows, r));
+}
+
+fp8idx_status check_shape(int32_t H, int32_t D) {
+  if (H != 32 || D != 128) return FP8IDX_EUNSUPPORTED;
+  return FP8IDX_OK;
+}
+
+fp8idx_status check_map(const fp8idx_map* map) {
+  if (map == nullptr) return FP8IDX_OK;
+  switch (map->kind) {
+    case FP8IDX_MAP_NONE:
+      return FP8IDX_OK;
+    case FP8IDX_MAP_TOKEN_TABLE:
+      if (!map->table || map->ld < 1 || map->num_req < 1) return FP8IDX_EINVAL;
+      if (!aligned(map->table, 4) || (map->cu_rows && !aligned(map->cu_rows, 4))) return FP8IDX_EINVAL;
+      return FP8IDX_OK;
+    case FP8IDX_MAP_BLOCK_TABLE:
+      if (!map->table || map->ld < 1 || map->num_req < 1 || map->rows_per_req < 1 || map->page_size < 1)
+        return FP8IDX_EINVAL;
+      if (!aligned(map->table, 4)) return FP8IDX_EINVAL;
+      return FP8IDX_OK;
+    default:
+      return FP8IDX_EINVAL;
+  }
+}
+
+fp8idx::TopkMap to_kernel_map(const fp8idx_map* map) {
+  fp8idx::TopkMap m{};
+  if (map == nullptr) {
+    m.kind = FP8IDX_MAP_NONE;
+    return m;
+  }
+  m.kind = map->kind;
+  m.table = map->table;
+  m.ld = map->ld;
+  m.num_req = map->num_req;
+  m.cu_rows = map->cu_rows;
+  m.rows_per_req = map->rows_per_req;
+  m.page_size = map->page_size;
+  return m;
+}
+
+fp8idx_status check_ragged(const uint8_t* q, const uint8_t* kv, const float* kv_scale, const float* weights,
+                           const int32_t* ks, const int32_t* ke, int32_t m, int32_t n, int32_t H, int32_t D) {
+  if (fp8idx_status s = check_shape(H, D)) return s;
+  if (m < 0 || n < 1) return FP8IDX_EINVAL;
+  if (m == 0) return FP8IDX_OK;
+  if (!q || !kv || !kv_scale || !weights || !ks || !ke) return FP8IDX_EINVAL;
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(weights, 16)) return FP8IDX_EINVAL;
+  if (!aligned(kv_scale, 4) || !aligned(ks, 4) || !aligned(ke, 4)) return FP8IDX_EINVAL;
+  return FP8IDX_OK;
+}
+
+fp8idx_status check_paged(const uint8_t* q, const uint8_t* kv_pool, const float* scale_pool,
+                          const float* weights, const int32_t* row_len, const int32_t* block_table,
+                          int32_t B, int32_t next_n, int32_t H, int32_t D, int32_t page_size,
+                          int32_t max_pages, int64_t num_pages, int32_t width) {
+  if (fp8idx_status s = check_shape(H, D)) return s;
+  if (page_size != 64) return FP8IDX_EUNSUPPORTED;
+  if (B < 0 || next_n < 1 || max_pages < 1 || num_pages < 1 || width < 0) return FP8IDX_EINVAL;
+  if ((int64_t)width > (int64_t)max_pages * page_size) return FP8IDX_EINVAL;
+  if (num_pages > (int64_t)(INT32_MAX / page_size)) return FP8IDX_EUNSUPPORTED;   // slot ids are int32
+  if ((int64_t)B * next_n > INT32_MAX) return FP8IDX_EINVAL;
+  if (B == 0) return FP8IDX_OK;
+  if (!q || !kv_pool || !scale_pool || !weights || !row_len || !block_table) return FP8IDX_EINVAL;
+  if (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(weights, 16)) return FP8IDX_EINVAL;
+  if (!aligned(scale_pool, 4) || !aligned(row_len, 4) || !aligned(block_table, 4)) return FP8IDX_EINVAL;
+  return FP8IDX_OK;
+}
+
+fp8idx_status check_topk_args(int32_t rows, int32_t width, int64_t ld, int32_t k, int64_t ld_out) {
+  if (k < 1 || k > fp8idx::kMaxK) return FP8IDX_EUNSUPPORTED;
+  if (rows < 0 || width < 0 || ld < width || ld < 1 || ld_out < k) return FP8IDX_EINVAL;
+  return FP8IDX_OK;
+}
+
+size_t fused_ws_bytes(int32_t rows, int64_t width, int32_t k, size_t cap, int32_t granule) {
+  const int64_t ld = ws_logits_ld(width);
+  int32_t rpc = rows_per_chunk(cap, ld, rows);
+  if (granule > 1 && rpc < rows) rpc = std::max<int32_t>(granule, rpc / granule * granule);
+  rpc = std::min(rpc, rows);
+  if (rpc <= 0) return 0;
+  const int32_t last = rows % rpc == 0 ? rpc : rows % rpc;
+  const size_t logits = align256((size_t)rpc * (size_t)ld * 4u);
+  const size_t t0 = fp8idx::topk_workspace_bytes(fp8idx::plan_topk(rpc, width, k));
+  const size_t t1 = fp8idx::topk_workspace_bytes(fp8idx::plan_topk(last, width, k));
+  return logits + std::max(t0, t1);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8idx_status_string(int32_t status) {
+  switch (status) {
+    case FP8IDX_OK: return "FP8IDX_OK";
+    case FP8IDX_EINVAL: return "FP8IDX_EINVAL: invalid argument (null pointer, size, stride or alignment)";
+    case FP8IDX_EUNSUPPORTED: return "FP8IDX_EUNSUPPORTED: unsupported shape (H must be 32, D 128, page size 64, 1 <= k <= 16384)";
+    case FP8IDX_EWORKSPACE: return "FP8IDX_EWORKSPACE: workspace smaller than fp8idx_workspace_bytes()";
+    case FP8IDX_EDEVICE: return "FP8IDX_EDEVICE: no gfx950 device is current";
+    case FP8IDX_EHIP: return "FP8IDX_EHIP: a HIP call failed (see fp8idx_last_hip_error)";
+    default: return "FP8IDX: unknown status";
+  }
+}
+
+int32_t fp8idx_last_hip_error(void) { return g_last_hip_error; }
+
+const char* fp8idx_version(void) { return "fp8idx 0.1.0 gfx950"; }
+
+int32_t fp8idx_rows_per_chunk(size_t logits_cap_bytes, int64_t width, int32_t rows) {
+  return rows_per_chunk(logits_cap_bytes, ws_logits_ld(width), rows);
+}
+
+size_t fp8idx_workspace_bytes(int32_t op, int32_t rows, int64_t width, int32_t k, size_t logits_cap_bytes) {
+  if (rows <= 0 || width < 0 || k < 1 || k > fp8idx::kMaxK) return 0;
+  switch (op) {
+    case FP8IDX_OP_TOPK:
+      return fp8idx::topk_workspace_bytes(fp8idx::plan_topk(rows, width, k));
+    case FP8IDX_OP_LOGITS_TOPK_RAGGED:
+      return fused_ws_bytes(rows, width, k, logits_cap_bytes, 1);
+    default:
+      return 0;
+  }
+}
+
+fp8idx_status indexer_logits_ragged(const uint8_t* q, const uint8_t* kv, const float* kv_scale,
+                                    const float* weights, const int32_t* ks, const int32_t* ke,
+                                    int32_t m, int32_t n, int32_t H, int32_t D,
+                                    float* logits, int64_t ld_logits, int32_t clean, void* stream) {
+  if (fp8idx_status s = check_ragged(q, kv, kv_scale, weights, ks, ke, m, n, H, D)) return s;
+  if (m > 0 && (!logits || !aligned(logits, 4) || ld_logits < n)) return FP8IDX_EINVAL;
+  if (m == 0) return FP8IDX_OK;
+  DeviceInfo dev;
+  if (fp8idx_status s = current_device(&dev)) return s;
+  fp8idx::RaggedLogitsArgs a{q, kv, kv_scale, weights, ks, ke, m, n, logits, ld_logits, clean};
+  const hipError_t e = fp8idx::launch_logits_ragged(a, dev, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8IDX_OK : hip_fail(e);
+}
+
+fp8idx_status indexer_logits_paged(const uint8_t* q, const uint8_t* kv_pool, const float* scale_pool,
+                                   const float* weights, const int32_t* row_len, const int32_t* block_table,
+                                   int32_t B, int32_t next_n, int32_t H, int32_t D, int32_t page_size,
+                                   int32_t max_pages, int64_t num_pages, float* logits, int64_t ld_logits,
+                                   int32_t width, int32_t clean, void* stream) {
+  if (fp8idx_status s = check_paged(q, kv_pool, scale_pool, weights, row_len, block_table, B, next_n, H, D,
+                                    page_size, max_pages, num_pages, width))
+    return s;
+  if (B > 0 && (!logits || !aligned(logits, 4) || ld_logits < width || ld_logits < 1)) return FP8IDX_EINVAL;
+  if (B == 0 || width == 0) return FP8IDX_OK;
+  DeviceInfo dev;
+  if (fp8idx_status s = current_device(&dev)) return s;
+  fp8idx::PagedLogitsArgs a{q, kv_pool, scale_pool, weights, row_len, block_table, B, next_n, max_pages,
+                            num_pages, logits, ld_logits, width, clean};
+  const hipError_t e = fp8idx::launch_logits_paged(a, dev, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8IDX_OK : hip_fail(e);
+}
+
+fp8idx_status indexer_topk(const float* logits, int64_t ld, int32_t rows, int32_t width, const int32_t* ks,
+                           const int32_t* ke, int32_t k, int32_t row0, const fp8idx_map* map, int32_t* out,
+                           int64_t ld_out, void* ws, size_t ws_bytes, void* stream) {
+  if (fp8idx_status s = check_topk_args(rows, width, ld, k, ld_out)) return s;
+  if (fp8idx_status s = check_map(map)) return s;
+  if (rows == 0) return FP8IDX_OK;
+  if (!logits || !ke || !out || row0 < 0) return FP8IDX_EINVAL;
+  if (!aligned(logits, 4) || !aligned(ke, 4) || !aligned(out, 4) || (ks && !aligned(ks, 4))) return FP8IDX_EINVAL;
+  const fp8idx::TopkPlan plan = fp8idx::plan_topk(rows, width, k);
+  const size_t need = fp8idx::topk_workspace_bytes(plan);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return FP8IDX_EWORKSPACE;
+  if (need > 0 && !aligned(ws, 256)) return FP8IDX_EINVAL;
+  DeviceInfo dev;
+  if (fp8idx_status s = current_device(&dev)) return s;
+  fp8idx::TopkArgs a{logits, ld, rows, width, ks, ke, k, row0, to_kernel_map(map), out, ld_out};
+  const hipError_t e = fp8idx::launch_topk(a, plan, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8IDX_OK : hip_fail(e);
+}
+
+fp8idx_status indexer_logits_topk_ragged(const uint8_t* q, const uint8_t* kv, const float* kv_scale,
+                                         const float* weights, const int32_t* ks, const int32_t* ke, int32_t m,
+                                         int32_t n, int32_t H, int32_t D, int32_t k, const fp8idx_map* map,
+                                         int32_t* out, int64_t ld_out, size_t logits_cap_bytes, void* ws,
+                                         size_t ws_bytes, void* stream) {
+  if (fp8idx_status s = check_ragged(q, kv, kv_scale, weights, ks, ke, m, n, H, D)) return s;
+  if (fp8idx_status s = check_topk_args(m, n, n, k, ld_out)) return s;
+  if (fp8idx_status s = check_map(map)) return s;
+  if (m == 0) return FP8IDX_OK;
+  if (!out || !aligned(out, 4)) return FP8IDX_EINVAL;
+  const size_t need = fused_ws_bytes(m, n, k, logits_cap_bytes, 1);
+  if (ws == nullptr || ws_bytes < need) return FP8IDX_EWORKSPACE;
+  if (!aligned(ws, 256)) return FP8IDX_EINVAL;
+  DeviceInfo dev;
+  if (fp8idx_status s = current_device(&dev)) return s;
+
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t ld = ws_logits_ld(n);
+  const int32_t rpc = rows_per_chunk(logits_cap_bytes, ld, m);
+  float* chunk_logits = static_cast<float*>(ws);
+  void* topk_ws = static_cast<uint8_t*>(ws) + align256((size_t)rpc * (size_t)ld * 4u);
+  const fp8idx::TopkMap kmap = to_kernel_map(map);
+  for (int32_t s0 = 0; s0 < m; s0 += rpc) {
+    const int32_t rows = std::min(rpc, m - s0);
+    fp8idx::RaggedLogitsArgs la{q + (size_t)s0 * fp8idx::kQRowBytesHost, kv, kv_scale,
+                                weights + (size_t)s0 * 32, ks + s0, ke + s0, rows, n, chunk_logits, ld, 0};
+    hipError_t e = fp8idx::launch_logits_ragged(la, dev, st);
+    if (e != hipSuccess) return hip_fail(e);
+    const fp8idx::TopkPlan plan = fp8idx::plan_topk(rows, n, k);
+    fp8idx::TopkArgs ta{chunk_logits, ld, rows, n, ks + s0, ke + s0, k, s0, kmap, out + (int64_t)s0 * ld_out, ld_out};
+    e = fp8idx::launch_topk(ta, plan, topk_ws, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return FP8IDX_OK;
+}
+
+fp8idx_status indexer_logits_topk_paged(const uint8_t* q, const uint8_t* kv_pool, const float* scale_pool,
+                                        const float* weights, const int32_t* row_len, const int32_t* block_table,
+                                        int32_t B, int32_t next_n, int32_t H, int32_t D, int32_t page_size,
+                                        int32_t max_pages, int64_t num_pages, int32_t width, int32_t k,
+                                        int32_t map_to_slots, int32_t* out, int64_t ld_out,
+                                        size_t logits_cap_bytes, void* ws, size_t ws_bytes, void* stream) {
+  if (fp8idx_status s = check_paged(q, kv_pool, scale_pool, weights, row_len, block_table, B, next_n, H, D,
+                                    page_size, max_pages, num_pages, width))
+    return s;
+  const int64_t rows64 = (int64_t)B * next_n;
+  const int32_t rows = (int32_t)rows64;
+  if (fp8idx_status s = check_topk_args(rows, width, std::max<int64_t>(width, 1), k, ld_out)) return s;
+  if (rows == 0) return FP8IDX_OK;
+  if (!out || !aligned(out, 4)) return FP8IDX_EINVAL;
+  const size_t need = fused_ws_bytes(rows, width, k, logits_cap_bytes, next_n);
+  if (ws == nullptr || ws_bytes < need) return FP8IDX_EWORKSPACE;
+  if (!aligned(ws, 256)) return FP8IDX_EINVAL;
+  DeviceInfo dev;
+  if (fp8idx_status s = current_device(&dev)) return s;
+
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t ld = ws_logits_ld(width);
+  int32_t rpc = rows_per_chunk(logits_cap_bytes, ld, rows);
+  if (rpc < rows) rpc = std::max<int32_t>(next_n, rpc / next_n * next_n);
+  rpc = std::min(rpc, rows);
+  const int32_t req_per_chunk = std::max<int32_t>(1, rpc / next_n);
+  float* chunk_logits = static_cast<float*>(ws);
+  void* topk_ws = static_cast<uint8_t*>(ws) + align256((size_t)rpc * (size_t)ld * 4u);
+  fp8idx::TopkMap kmap{};
+  if (map_to_slots) {
+    kmap.kind = FP8IDX_MAP_BLOCK_TABLE;
+    kmap.table = block_table;
+    kmap.ld = max_pages;
+    kmap.num_req = B;
+    kmap.rows_per_req = next_n;
+    kmap.page_size = page_size;
+  } else {
+    kmap.kind = FP8IDX_MAP_NONE;
+  }
+  for (int32_t b0 = 0; b0 < B; b0 += req_per_chunk) {
+    const int32_t nb = std::min(req_per_chunk, B - b0);
+    const int32_t r0 = b0 * next_n;
+    const int32_t nr = nb * next_n;
+    fp8idx::PagedLogitsArgs la{q + (size_t)r0 * fp8idx::kQRowBytesHost, kv_pool, scale_pool,
+                               weights + (size_t)r0 * 32, row_len + r0, block_table + (int64_t)b0 * max_pages,
+                               nb, next_n, max_pages, num_pages, chunk_logits, ld, width, 0};
+    hipError_t e = fp8idx::launch_logits_paged(la, dev, st);
+    if (e != hipSuccess) return hip_fail(e);
+    const fp8idx::TopkPlan plan = fp8idx::plan_topk(nr, width, k);
+    fp8idx::TopkArgs ta{chunk_logits, ld, nr, width, nullptr, row_len + r0, k, r0, kmap,
+                        out + (int64_t)r0 * ld_out, ld_out};
+    e = fp8idx::launch_topk(ta, plan, topk_ws, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return FP8IDX_OK;
+}
+
+size_t fp8idx_workspace_bytes_paged(int32_t B, int32_t next_n, int32_t width, int32_t k, size_t logits_cap_bytes) {
+  if (B <= 0 || next_n <= 0 || width < 0 || k < 1 || k > fp8idx::kMaxK) return 0;
+  return fused_ws_bytes(B * next_n, width, k, logits_cap_bytes, next_n);
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8idx {
+
+struct RaggedLogitsArgs {
+  const uint8_t* q;
+  const uint8_t* kv;
+  const float* kv_scale;
+  const float* weights;
+  const int32_t* ks;
+  const int32_t* ke;
+  int32_t m;
+  int32_t n;
+  float* logits;
+  int64_t ld;
+  int32_t clean;
+};
+
+struct PagedLogitsArgs {
+  const uint8_t* q;
+  const uint8_t* kv_pool;
+  const float* scale_pool;
+  const float* weights;
+  const int32_t* row_len;
+  const int32_t* block_table;
+  int32_t B;
+  int32_t next_n;
+  int32_t max_pages;
+  int64_t num_pages;
+  float* logits;
+  int64_t ld;
+  int32_t width;
+  int32_t clean;
+};
+
+struct TopkMap {
+  int32_t kind;
+  const int32_t* table;
+  int64_t ld;
+  int32_t num_req;
+  const int32_t* cu_rows;
+  int32_t rows_per_req;
+  int32_t page_size;
+};
+
+struct TopkArgs {
+  const float* logits;
+  int64_t ld;
+  int32_t rows;
+  int32_t width;
+  const int32_t* ks;  // may be null
+  const int32_t* ke;
+  int32_t k;
+  int32_t row0;
+  TopkMap map;
+  int32_t* out;
+  int64_t ld_out;
+};
+
+// Host-side plan of the multi-level top-k: level 0 splits each row into
+// segments; each further level merges the previous level's per-segment
+// candidates until one segment per row remains.
+struct TopkLevel {
+  int64_t in_len;   // elements per row entering this level
+  int32_t seg_len;  // elements per segment (<= capacity of the chosen config)
+  int32_t nseg;     // segments per row
+  int32_t cfg;      // kernel configuration id
+};
+
+constexpr int kMaxTopkLevels = 8;
+constexpr size_t kQRowBytesHost = 32 * 128;   // q bytes per query row (H * D)
+constexpr int kMaxK = 16384;
+
+struct TopkPlan {
+  int nlevels;
+  TopkLevel level[kMaxTopkLevels];
+  size_t buf_bytes[2];  // ping-pong candidate buffers (bytes each)
+};
+
+// Device properties the launchers need, cached per device.
+struct DeviceInfo {
+  int cu_count;
+};
+
+TopkPlan plan_topk(int32_t rows, int64_t width, int32_t k);
+size_t topk_workspace_bytes(const TopkPlan& p);
+
+hipError_t launch_logits_ragged(const RaggedLogitsArgs& a, const DeviceInfo& dev, hipStream_t s);
+hipError_t launch_logits_paged(const PagedLogitsArgs& a, const DeviceInfo& dev, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, const TopkPlan& plan, void* ws, hipStream_t s);
+
+}  // namespace fp8idx

@@ -1,0 +1,199 @@
+// Ragged-prefill fp8 MQA logits for gfx950.
+//
+//   logits[i, j] = sum_h w[i, h] * max(dot(q[i, h, :], kv[j, :]) * kv_scale[j], 0),  ks[i] <= j < ke[i]
+//
+// (the `fp8_mqa_logits(q, (kv, kv_scales), weights, ks, ke, clean_logits)` call of
+// the indexer loop on the bench_mqa_logits_chunking.py page).
+//
+// Work decomposition
+// - A workgroup owns kRows = 4 * WAVES consecutive query rows and one slice of
+//   the keys ("split"); each of its waves owns 4 query rows.  The 4 rows x 32
+//   heads x 128 bytes of q of a wave live in VGPRs for the whole kernel as
+//   eight 16x16x128 MFMA A-operands, next to the matching weights.
+// - Keys stream through LDS in tiles of 64 keys x 128 bytes (8 KiB, double
+//   buffered), loaded with coalesced 16-byte global loads.  Inside a row the
+//   16-byte chunks are XOR-swizzled by (key & 7) so that the B-operand reads
+//   (lane l: key l % 16, bytes 32 * (l / 16) .. +32) hit distinct banks.
+// - Per 16-key fragment a wave issues 8 MFMAs (4 rows x 2 head tiles of 16);
+//   each lane then holds 8 heads of one (row, key) score set.  ReLU and the
+//   head weights are applied in registers (max + fma per score), the four
+//   16-lane rows are combined with permlane32/permlane16 swaps so that every
+//   lane ends with one finished (row, key) logit, which is scaled by
+//   kv_scale[j] (factored out of the head sum: valid because kv_scale >= 0)
+//   and stored.  The per-head scores never leave registers.
+// - Tiles outside the union of the workgroup's row windows are skipped; only
+//   the partially covered edge tile is masked element by element.
+
+#include "device_common.hpp"
+#include "launch.hpp"
+#include "mqa_core.hpp"
+
+namespace fp8idx {
+
+constexpr int kTileKeys = 64;
+
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 2) void logits_ragged_kernel(RaggedLogitsArgs a, int splits,
+                                                                       int keys_per_split) {
+  constexpr int kThreads = 64 * WAVES;
+  constexpr int kRows = 4 * WAVES;
+  constexpr int kChunks = kTileKeys * (kDim / 16);   // 16-byte chunks per tile
+  constexpr int kChunksPerThread = kChunks / kThreads;
+  static_assert(kChunks % kThreads == 0, "tile chunks must divide the workgroup");
+
+  __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][kTileKeys * kDim];
+  __shared__ float s_scale[2][kTileKeys];
+  __shared__ int s_ks[kRows];
+  __shared__ int s_ke[kRows];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rb = blockIdx.x / splits;
+  const int split = blockIdx.x - rb * splits;
+  const int row0 = rb * kRows;
+  const int n = a.n;
+
+  if (tid < kRows) {
+    const int r = row0 + tid;
+    int s = 0, e = 0;
+    if (r < a.m) {
+      e = min(max(a.ke[r], 0), n);
+      s = min(max(a.ks[r], 0), e);
+    }
+    s_ks[tid] = s;
+    s_ke[tid] = e;
+  }
+  __syncthreads();
+
+  int lo = n, hi = 0;
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const int s = s_ks[i], e = s_ke[i];
+    if (e > s) {
+      lo = min(lo, s);
+      hi = max(hi, e);
+    }
+  }
+  const int split_lo = split * keys_per_split;
+  const int split_hi = min(n, split_lo + keys_per_split);
+  const int klo = max(lo, split_lo);
+  const int khi = min(hi, split_hi);
+  int tile_lo = split_lo, tile_end = split_lo;   // computed range [tile_lo, tile_end)
+  int ntiles = 0;
+  if (klo < khi) {
+    tile_lo = max(split_lo, klo & ~(kTileKeys - 1));
+    ntiles = (khi - tile_lo + kTileKeys - 1) / kTileKeys;
+    tile_end = min(split_hi, tile_lo + ntiles * kTileKeys);
+  }
+  const int rows_here = min(kRows, a.m - row0);
+
+  if (a.clean) {
+    // -inf over the split's columns that no tile below covers
+    const int w0 = tile_lo - split_lo;
+    const int w1 = split_hi - tile_end;
+    for (int r = 0; r < rows_here; ++r) {
+      float* out = a.logits + (int64_t)(row0 + r) * a.ld;
+      for (int c = tid; c < w0; c += kThreads) out[split_lo + c] = -INFINITY;
+      for (int c = tid; c < w1; c += kThreads) out[tile_end + c] = -INFINITY;
+    }
+  }
+  if (ntiles == 0) return;
+
+  // q fragments and weights of this wave's 4 rows
+  QFrags qf;
+#pragma unroll
+  for (int qi = 0; qi < 4; ++qi) {
+    const int row = row0 + 4 * wave + qi;
+    const bool ok = row < a.m;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      qf.a[qi][t] = load_q_frag(a.q, row, ok, t, lane);
+      qf.w[qi][t] = load_w4(a.weights, row, ok, t, lane);
+    }
+  }
+  const int my_r = 4 * wave + reduce_rows4_qsel(lane);
+  const int my_row = row0 + my_r;
+  const bool row_ok = my_row < a.m;
+  const int my_ks = s_ks[my_r];
+  const int my_ke = s_ke[my_r];
+  float* __restrict__ out_row = a.logits + (int64_t)(row_ok ? my_row : 0) * a.ld;
+  const bool clean = a.clean != 0;
+
+  v4i stage[kChunksPerThread];
+  float stage_scale = 0.f;
+  auto gload = [&](int tile) {
+#pragma unroll
+    for (int c = 0; c < kChunksPerThread; ++c) {
+      const int ci = tid + c * kThreads;
+      const int key = ci >> 3;
+      const int j = tile + key;
+      v4i v = {0, 0, 0, 0};
+      if (j < n) v = *reinterpret_cast<const v4i*>(a.kv + (size_t)j * kDim + (ci & 7) * 16);
+      stage[c] = v;
+    }
+    if (tid < kTileKeys) {
+      const int j = tile + tid;
+      stage_scale = j < n ? a.kv_scale[j] : 0.f;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < kChunksPerThread; ++c) {
+      const int ci = tid + c * kThreads;
+      const int key = ci >> 3;
+      *reinterpret_cast<v4i*>(&s_kv[buf][key * kDim + (((ci & 7) ^ (key & 7)) * 16)]) = stage[c];
+    }
+    if (tid < kTileKeys) s_scale[buf][tid] = stage_scale;
+  };
+
+  gload(tile_lo);
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int tile = tile_lo + it * kTileKeys;
+    lstore(buf);
+    __syncthreads();
+    if (it + 1 < ntiles) gload(tile + kTileKeys);
+#pragma unroll
+    for (int f = 0; f < kTileKeys / 16; ++f) {
+      const int key = f * 16 + (lane & 15);
+      const uint8_t* base = &s_kv[buf][key * kDim];
+      const int c0 = (2 * (lane >> 4)) ^ (key & 7);
+      const int c1 = (2 * (lane >> 4) + 1) ^ (key & 7);
+      const v4i b0 = *reinterpret_cast<const v4i*>(base + c0 * 16);
+      const v4i b1 = *reinterpret_cast<const v4i*>(base + c1 * 16);
+      const v8i b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      const float v = fragment_logit(qf, b) * s_scale[buf][key];
+      const int j = tile + key;
+      if (row_ok && j < tile_end) {
+        if (j >= my_ks && j < my_ke) {
+          out_row[j] = v;
+        } else if (clean) {
+          out_row[j] = -INFINITY;
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_logits_ragged(const RaggedLogitsArgs& a, const DeviceInfo& dev, hipStream_t s) {
+  if (a.m <= 0) return hipSuccess;
+  constexpr int kWaves = 4;
+  constexpr int kRows = 4 * kWaves;
+  const int64_t row_blocks = (a.m + kRows - 1) / kRows;
+  const int64_t target = 4LL * (dev.cu_count > 0 ? dev.cu_count : 256);
+  int64_t splits = (target + row_blocks - 1) / row_blocks;
+  const int64_t max_splits = a.n / 2048 > 0 ? a.n / 2048 : 1;
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  int64_t kps = (a.n + splits - 1) / splits;
+  kps = (kps + kTileKeys - 1) / kTileKeys * kTileKeys;
+  splits = (a.n + kps - 1) / kps;
+  const int64_t grid = row_blocks * splits;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(logits_ragged_kernel<kWaves>, dim3((unsigned)grid), dim3(64 * kWaves), 0, s, a,
+                     (int)splits, (int)kps);
+  return hipGetLastError();
+}
+
+}  // namespace fp8idx

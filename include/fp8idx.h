@@ -1,0 +1,241 @@
+/*
+ * fp8idx — fp8 MQA indexer logits + top-k for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of the sparse-attention indexer hot path:
+ *
+ *   logits[i, j] = sum_h weights[i, h] * max(dot(q[i, h, :], kv[j, :]) * kv_scale[j], 0)
+ *                  for ks[i] <= j < ke[i]  (-inf elsewhere when `clean` is set)
+ *
+ * followed by the per-row indices of the k largest logits inside [ks, ke),
+ * mapped through a page table.  The operations are the two library calls of
+ * the indexer loop on the bench_mqa_logits_chunking.py page
+ * (`fp8_mqa_logits(q, (kv, kv_scales), weights, ks, ke, clean_logits)` and
+ * `fast_topk_transform_fused(score, lengths, page_table_size_1, cu_seqlens_q,
+ * topk, row_starts)`), the paged-decode logits named on the vessl-ai/sglang
+ * PR #87 page, and the row-chunked loop of the chunking page that bounds the
+ * rows x keys float32 logits buffer by a byte cap.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Shapes: q has H = 32 heads of D = 128 fp8 e4m3fn (OCP "fn" flavour) bytes.
+ *   Other H or D return FP8IDX_EUNSUPPORTED.
+ * - Pointers: every array pointer is a DEVICE pointer (HIP device memory or
+ *   memory the device can read) unless marked "host".  The caller owns all
+ *   memory.  The library never allocates, frees or keeps device memory between
+ *   calls; scratch comes only from the caller's `ws` buffer.
+ * - Layouts: row-major, contiguous in the last dimension; leading dimensions
+ *   (in elements) are explicit where a buffer may be wider than its content.
+ *   q, kv and kv pools must be 16-byte aligned; float and int32 arrays 4-byte
+ *   aligned; `ws` 256-byte aligned.
+ * - Execution: work is enqueued on `stream` (a hipStream_t; NULL = the legacy
+ *   default stream) and the call returns without waiting.  No call allocates,
+ *   synchronises the host, or copies host memory to the device, so every entry
+ *   point can be captured in a HIP graph.
+ * - Errors: arguments are validated on the host before anything is enqueued.
+ *   On any status other than FP8IDX_OK nothing was enqueued and no output was
+ *   written.  FP8IDX_EHIP means a HIP call failed (the HIP error is reported
+ *   by fp8idx_last_hip_error()).
+ * - Device-side contents (ks, ke, row lengths, table entries) are not read by
+ *   the host.  Kernels clamp them so that no access leaves the buffers the
+ *   sizes describe: ke is clamped to the key count, ks to [0, ke], row lengths
+ *   to the logits width, and table entries outside their range map to -1 (or,
+ *   for kv pages, make the affected keys' logits -inf).  Results for such
+ *   out-of-contract inputs are otherwise unspecified.
+ * - kv_scale must be >= 0 (quantisation scales); NaN or infinite inputs give
+ *   unspecified results.
+ * - Determinism: identical inputs give identical output bytes.  Concurrent
+ *   calls on different streams are safe when their outputs and workspaces do
+ *   not overlap.
+ * - Top-k output: each row holds the selected keys (a set: positions within
+ *   the row are not part of the contract; this library writes them in
+ *   ascending key order) followed by -1 padding when the row's window holds
+ *   fewer than k keys.  A tie at the k-th value is broken toward the lower key
+ *   index, so the selected set is unique.
+ */
+#ifndef FP8IDX_H
+#define FP8IDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define FP8IDX_API __attribute__((visibility("default")))
+#else
+#define FP8IDX_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp8idx_status {
+  FP8IDX_OK = 0,
+  FP8IDX_EINVAL = 1,       /* null pointer, bad size, stride or alignment */
+  FP8IDX_EUNSUPPORTED = 2, /* H != 32, D != 128, k out of range, page size not 64 */
+  FP8IDX_EWORKSPACE = 3,   /* ws_bytes smaller than the matching *_workspace_bytes() */
+  FP8IDX_EDEVICE = 4,      /* no device, or the current device is not gfx950 */
+  FP8IDX_EHIP = 5          /* a HIP launch or query failed */
+} fp8idx_status;
+
+/* Index map applied by the top-k stage (the "transform" of the chunking page's
+ * fast_topk_transform_fused). */
+typedef enum fp8idx_map_kind {
+  FP8IDX_MAP_NONE = 0,        /* output the raw key index j */
+  FP8IDX_MAP_TOKEN_TABLE = 1, /* page size 1: table[req(i) * ld + (j - ks[i])] */
+  FP8IDX_MAP_BLOCK_TABLE = 2  /* table[b * ld + j / page_size] * page_size + j % page_size,
+                                 b = i / rows_per_req (paged decode: physical slot id) */
+} fp8idx_map_kind;
+
+/* Host struct; the pointers inside are device pointers. */
+typedef struct fp8idx_map {
+  int32_t kind;            /* fp8idx_map_kind */
+  const int32_t* table;    /* [num_req, ld] int32; unused for FP8IDX_MAP_NONE */
+  int64_t ld;              /* table row stride in elements (>= 1) */
+  int32_t num_req;         /* rows of `table` */
+  const int32_t* cu_rows;  /* token table: [num_req + 1] row offsets of each request
+                              (like cu_seqlens_q); NULL puts every row in request 0 */
+  int32_t rows_per_req;    /* block table: consecutive rows per request (next_n) */
+  int32_t page_size;       /* block table: keys per page */
+} fp8idx_map;
+
+/* Operation selector for fp8idx_workspace_bytes(). */
+typedef enum fp8idx_op {
+  FP8IDX_OP_TOPK = 0,              /* indexer_topk */
+  FP8IDX_OP_LOGITS_TOPK_RAGGED = 1 /* indexer_logits_topk_ragged */
+} fp8idx_op;
+
+/*
+ * Ragged-prefill fp8 MQA logits (the chunking page's
+ * `fp8_mqa_logits(q, (kv, kv_scales), weights, ks, ke, clean_logits)`).
+ *
+ *   q        [m, H, D] uint8 e4m3fn      kv       [n, D] uint8 e4m3fn
+ *   kv_scale [n] float32 (>= 0)          weights  [m, H] float32
+ *   ks, ke   [m] int32: row i's key window is [ks[i], ke[i])
+ *   logits   [m, ld_logits] float32 output, ld_logits >= n.  Columns
+ *            [0, n) of every row are written when clean != 0 (-inf outside
+ *            the window); when clean == 0 only the window is guaranteed and
+ *            other columns < n hold unspecified values.  Columns >= n are
+ *            never touched.
+ * m == 0 is a no-op.  Requires n >= 1, m >= 0.
+ */
+FP8IDX_API fp8idx_status indexer_logits_ragged(const uint8_t* q, const uint8_t* kv, const float* kv_scale,
+                                    const float* weights, const int32_t* ks, const int32_t* ke,
+                                    int32_t m, int32_t n, int32_t H, int32_t D,
+                                    float* logits, int64_t ld_logits, int32_t clean,
+                                    void* stream);
+
+/*
+ * Paged-decode fp8 MQA logits (the paged form of the indexer named on the
+ * vessl-ai/sglang PR #87 page).  B requests of next_n query rows each; row
+ * r = b * next_n + t belongs to request b and sees keys [0, row_len[r]).
+ * Key j of request b lives in physical page block_table[b * max_pages + j / page_size],
+ * slot j % page_size.  The work split over keys is derived on the device from
+ * row_len; nothing is read back to the host.
+ *
+ *   q           [B, next_n, H, D] uint8     kv_pool    [num_pages, page_size, D] uint8
+ *   scale_pool  [num_pages, page_size] f32  weights    [B * next_n, H] float32
+ *   row_len     [B * next_n] int32          block_table [B, max_pages] int32
+ *   logits      [B * next_n, ld_logits] float32, width <= ld_logits columns
+ *               are owned by the call: row r's window [0, min(row_len[r], width))
+ *               is written, and with clean != 0 the rest of [0, width) is -inf.
+ * page_size must be 64.
+ */
+FP8IDX_API fp8idx_status indexer_logits_paged(const uint8_t* q, const uint8_t* kv_pool,
+                                   const float* scale_pool, const float* weights,
+                                   const int32_t* row_len, const int32_t* block_table,
+                                   int32_t B, int32_t next_n, int32_t H, int32_t D,
+                                   int32_t page_size, int32_t max_pages, int64_t num_pages,
+                                   float* logits, int64_t ld_logits, int32_t width,
+                                   int32_t clean, void* stream);
+
+/*
+ * Per-row top-k over float32 logits with the index map (the chunking page's
+ * `fast_topk_transform_fused(score, lengths=ke, page_table, cu_seqlens_q, topk,
+ * row_starts=ks)`).
+ *
+ *   logits [rows, ld] float32; row i's candidates are columns [ks[i], ke[i])
+ *          (ks NULL means 0; ke is clamped to `width` <= ld)
+ *   row0   global id of logits row 0, used by the map (request lookup)
+ *   map    host pointer; NULL means FP8IDX_MAP_NONE.  For the token table
+ *          ks must be indexed like the logits rows.
+ *   out    [rows, ld_out] int32, ld_out >= k: columns [0, k) are written
+ *   ws     device scratch of at least fp8idx_workspace_bytes(FP8IDX_OP_TOPK,
+ *          rows, width, k, 0) bytes (rows longer than one selection segment,
+ *          or few rows, are split into segments whose candidates live there;
+ *          the size may be 0, and ws may then be NULL)
+ * 1 <= k <= 16384.
+ */
+FP8IDX_API fp8idx_status indexer_topk(const float* logits, int64_t ld, int32_t rows, int32_t width,
+                           const int32_t* ks, const int32_t* ke, int32_t k, int32_t row0,
+                           const fp8idx_map* map, int32_t* out, int64_t ld_out,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Fused ragged logits + top-k under a logits byte cap (the row-chunked loop
+ * of the chunking page: rows per chunk = max(1, floor(cap / (n * 4)))).  Per
+ * chunk: logits into the workspace, then top-k into `out`, on one stream.
+ * The full rows x n buffer is never materialised unless the cap allows it.
+ *
+ *   logits_cap_bytes   0 = one chunk holding every row
+ *   ws, ws_bytes       >= fp8idx_workspace_bytes(FP8IDX_OP_LOGITS_TOPK_RAGGED,
+ *                        m, n, k, logits_cap_bytes)
+ * Other arguments as indexer_logits_ragged and indexer_topk (row0 = 0).
+ */
+FP8IDX_API fp8idx_status indexer_logits_topk_ragged(const uint8_t* q, const uint8_t* kv,
+                                         const float* kv_scale, const float* weights,
+                                         const int32_t* ks, const int32_t* ke,
+                                         int32_t m, int32_t n, int32_t H, int32_t D,
+                                         int32_t k, const fp8idx_map* map,
+                                         int32_t* out, int64_t ld_out,
+                                         size_t logits_cap_bytes, void* ws, size_t ws_bytes,
+                                         void* stream);
+
+/*
+ * Fused paged logits + top-k.  Output indices are physical kv slots
+ * (block_table[b, j / 64] * 64 + j % 64) when map_to_slots != 0, else raw key
+ * positions j.  `width` bounds every row length (the logits row stride used in
+ * the workspace).  Requests are chunked so that at most logits_cap_bytes of
+ * logits exist at once (0 = all rows at once).
+ *   ws_bytes >= fp8idx_workspace_bytes_paged(B, next_n, width, k, logits_cap_bytes)
+ * Chunks hold whole requests: at least one request per chunk even when one
+ * request's next_n rows exceed the cap.
+ */
+FP8IDX_API fp8idx_status indexer_logits_topk_paged(const uint8_t* q, const uint8_t* kv_pool,
+                                        const float* scale_pool, const float* weights,
+                                        const int32_t* row_len, const int32_t* block_table,
+                                        int32_t B, int32_t next_n, int32_t H, int32_t D,
+                                        int32_t page_size, int32_t max_pages, int64_t num_pages,
+                                        int32_t width, int32_t k, int32_t map_to_slots,
+                                        int32_t* out, int64_t ld_out,
+                                        size_t logits_cap_bytes, void* ws, size_t ws_bytes,
+                                        void* stream);
+
+/* Bytes of device workspace an operation needs (0 when it needs none).
+ * rows = logits rows (m or B * next_n), width = keys per row (n or the
+ * paged width).  Pure host arithmetic. */
+FP8IDX_API size_t fp8idx_workspace_bytes(int32_t op, int32_t rows, int64_t width, int32_t k,
+                              size_t logits_cap_bytes);
+
+/* Bytes of workspace indexer_logits_topk_paged needs.  Pure host arithmetic. */
+FP8IDX_API size_t fp8idx_workspace_bytes_paged(int32_t B, int32_t next_n, int32_t width, int32_t k,
+                                    size_t logits_cap_bytes);
+
+/* Rows per chunk of the fused ragged entry: max(1, floor(cap / (ld * 4))),
+ * capped at rows, where ld = width rounded up to a multiple of 4 (the row
+ * stride of the workspace logits); cap 0 gives rows.  Pure host arithmetic. */
+FP8IDX_API int32_t fp8idx_rows_per_chunk(size_t logits_cap_bytes, int64_t width, int32_t rows);
+
+/* Static string naming a status. */
+FP8IDX_API const char* fp8idx_status_string(int32_t status);
+
+/* The hipError_t of the last FP8IDX_EHIP returned on this thread (0 if none). */
+FP8IDX_API int32_t fp8idx_last_hip_error(void);
+
+/* Library version, e.g. "fp8idx 0.1.0 gfx950". */
+FP8IDX_API const char* fp8idx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8IDX_H */

@@ -1,0 +1,158 @@
+"""The C ABI without a GPU: every declared symbol is exported, host-side validation
+returns the documented status before touching any pointer, and the workspace /
+chunking arithmetic follows the chunking page's formula."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_mqa_logits_amd as F
+from fp8_mqa_logits_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8idx.h")
+
+OK, EINVAL, EUNSUP, EWS, EDEV, EHIP = 0, 1, 2, 3, 4, 5
+P = 1 << 20          # an aligned non-null fake device address; validation never dereferences it
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from fp8_mqa_logits_amd.build import build
+        build()
+    return F.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"FP8IDX_API\s+[\w\s\*]+?\b((?:indexer|fp8idx)_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) == 11, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(binding.EXPORTED) == names
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.fp8idx_status_string(s).decode().startswith("FP8IDX")
+    assert b"unknown" in lib.fp8idx_status_string(99)
+    assert lib.fp8idx_version().decode().startswith("fp8idx")
+
+
+def _ragged(lib, q=P, kv=P, sc=P, w=P, ks=P, ke=P, m=4, n=64, H=32, D=128, lg=P, ld=64, clean=1):
+    return lib.indexer_logits_ragged(q, kv, sc, w, ks, ke, m, n, H, D, lg, ld, clean, None)
+
+
+def test_ragged_validation(lib):
+    assert _ragged(lib, H=16) == EUNSUP
+    assert _ragged(lib, D=64) == EUNSUP
+    assert _ragged(lib, q=NULL) == EINVAL
+    assert _ragged(lib, ke=NULL) == EINVAL
+    assert _ragged(lib, lg=NULL) == EINVAL
+    assert _ragged(lib, q=P + 8) == EINVAL        # q must be 16-byte aligned
+    assert _ragged(lib, w=P + 4) == EINVAL        # weights are read as float4
+    assert _ragged(lib, ks=P + 2) == EINVAL
+    assert _ragged(lib, ld=63) == EINVAL          # ld < n
+    assert _ragged(lib, m=-1) == EINVAL
+    assert _ragged(lib, n=0) == EINVAL
+    assert _ragged(lib, m=0, q=NULL, lg=NULL) == OK   # empty call is a no-op
+    # valid arguments but no gfx950 device in this process
+    assert _ragged(lib) == EDEV
+
+
+def _paged(lib, q=P, pool=P, sp=P, w=P, rl=P, bt=P, B=2, nn=4, H=32, D=128, page=64, maxp=4, npages=10,
+           lg=P, ld=256, width=256, clean=1):
+    return lib.indexer_logits_paged(q, pool, sp, w, rl, bt, B, nn, H, D, page, maxp, npages, lg, ld, width,
+                                    clean, None)
+
+
+def test_paged_validation(lib):
+    assert _paged(lib, page=32) == EUNSUP
+    assert _paged(lib, H=64) == EUNSUP
+    assert _paged(lib, width=257) == EINVAL       # past max_pages * page_size
+    assert _paged(lib, ld=128) == EINVAL
+    assert _paged(lib, nn=0) == EINVAL
+    assert _paged(lib, bt=NULL) == EINVAL
+    assert _paged(lib, pool=P + 4) == EINVAL
+    assert _paged(lib, npages=1 << 26) == EUNSUP  # slot ids would not fit int32
+    assert _paged(lib, B=0, q=NULL) == OK
+    assert _paged(lib) == EDEV
+
+
+def _topk(lib, lg=P, ld=100, rows=3, width=100, ks=P, ke=P, k=10, row0=0, mp=None, out=P, ldo=10,
+          ws=None, wsb=0):
+    return lib.indexer_topk(lg, ld, rows, width, ks, ke, k, row0, mp, out, ldo, ws, wsb, None)
+
+
+def test_topk_validation(lib):
+    assert _topk(lib, k=0) == EUNSUP
+    assert _topk(lib, k=16385) == EUNSUP
+    assert _topk(lib, ldo=9) == EINVAL
+    assert _topk(lib, width=101) == EINVAL
+    assert _topk(lib, ke=NULL) == EINVAL
+    assert _topk(lib, ks=NULL) == EDEV            # ks is optional
+    bad = binding._CMap()
+    bad.kind = 7
+    assert _topk(lib, mp=ctypes.byref(bad)) == EINVAL
+    tok = binding._CMap()
+    tok.kind = binding.MAP_TOKEN_TABLE
+    assert _topk(lib, mp=ctypes.byref(tok)) == EINVAL     # no table
+    tok.table, tok.ld, tok.num_req = P, 8, 2
+    assert _topk(lib, mp=ctypes.byref(tok)) == EDEV
+    blk = binding._CMap()
+    blk.kind, blk.table, blk.ld, blk.num_req, blk.rows_per_req, blk.page_size = binding.MAP_BLOCK_TABLE, P, 4, 2, 0, 64
+    assert _topk(lib, mp=ctypes.byref(blk)) == EINVAL     # rows_per_req < 1
+    # a split plan needs workspace: few rows of a long window
+    need = lib.fp8idx_workspace_bytes(binding.OP_TOPK, 2, 200000, 2048, 0)
+    assert need > 0
+    assert _topk(lib, rows=2, ld=200000, width=200000, k=2048, ldo=2048) == EWS
+    assert _topk(lib, rows=2, ld=200000, width=200000, k=2048, ldo=2048, ws=P + 64, wsb=need) == EINVAL
+    assert _topk(lib, rows=2, ld=200000, width=200000, k=2048, ldo=2048, ws=P, wsb=need) == EDEV
+
+
+def test_fused_validation(lib):
+    f = lib.indexer_logits_topk_ragged
+    args = [P, P, P, P, P, P, 10, 1000, 32, 128, 64, None, P, 64, 0, P, 0, None]
+    need = lib.fp8idx_workspace_bytes(binding.OP_LOGITS_TOPK_RAGGED, 10, 1000, 64, 0)
+    assert need >= 10 * 1000 * 4
+    assert f(*args) == EWS
+    args[16] = need
+    assert f(*args) == EDEV
+    args[15] = P + 16
+    assert f(*args) == EINVAL                    # workspace must be 256-byte aligned
+    g = lib.indexer_logits_topk_paged
+    pargs = [P, P, P, P, P, P, 2, 4, 32, 128, 64, 4, 10, 256, 64, 1, P, 64, 0, P, 0, None]
+    assert g(*pargs) == EWS
+    pargs[20] = lib.fp8idx_workspace_bytes_paged(2, 4, 256, 64, 0)
+    assert g(*pargs) == EDEV
+
+
+def test_rows_per_chunk_follows_chunking_page(lib):
+    # rows per chunk = max(1, int(gb * 1e9) // (n * 4)); n is a multiple of 4 in all of these
+    assert F.fp8idx_rows_per_chunk(2_000_000_000, 210000, 7500) == 2380
+    assert F.fp8idx_rows_per_chunk(2_000_000_000, 65536, 8192) == 7629
+    assert F.fp8idx_rows_per_chunk(8_000_000_000, 65536, 8192) == 8192
+    assert F.fp8idx_rows_per_chunk(500_000_000, 150000 + 4096, 512) == 512
+    assert F.fp8idx_rows_per_chunk(1, 65536, 8192) == 1
+    assert F.fp8idx_rows_per_chunk(0, 65536, 8192) == 8192
+    # non-multiple of 4: the workspace row stride is rounded up to 4 floats
+    assert F.fp8idx_rows_per_chunk(4004 * 4 * 10, 4001, 100) == 10
+
+
+def test_fused_workspace_covers_chunk_and_candidates(lib):
+    cap = 2_000_000_000
+    ws = F.fp8idx_workspace_bytes(F.OP_LOGITS_TOPK_RAGGED, 7500, 210000, 2048, cap)
+    logits = 2380 * 210000 * 4
+    cand = 2380 * 4 * 2048 * 8          # 4 segments of up to 52500 keys per row
+    assert ws >= logits + cand
+    assert ws <= logits + cand + 4096
+    # one-shot on 8192 x 65536: the full 2 GiB buffer, single-segment top-k
+    assert F.fp8idx_workspace_bytes(F.OP_LOGITS_TOPK_RAGGED, 8192, 65536, 2048, 0) == 8192 * 65536 * 4

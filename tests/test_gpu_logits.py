@@ -1,0 +1,182 @@
+"""Parity of the HIP logits kernels (ragged prefill and paged decode) with the float64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_mqa_logits_amd as F
+from oracle import mqa_logits, paged_mqa_logits
+from tests.parity import assert_logits_close, cancellation_tol, to_dev
+from workloads.generate import H, D, ragged_inputs, multi_request_ragged, paged_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _ragged_dev(inp):
+    return [to_dev(a) for a in (inp.q, inp.kv, inp.kv_scale, inp.weights, inp.ks, inp.ke)]
+
+
+def _run_ragged(inp, clean=True, ld=None):
+    q, kv, sc, w, ks, ke = _ragged_dev(inp)
+    out = None
+    if ld is not None:
+        out = torch.full((inp.m, ld), 12345.0, dtype=torch.float32, device="cuda")
+    g = F.indexer_logits_ragged(q, kv, sc, w, ks, ke, clean=clean, logits=out)
+    torch.cuda.synchronize()
+    return g.cpu().numpy()
+
+
+def test_tiny_config_all_rows():
+    inp = ragged_inputs(64, 4096, 512, seed=1)
+    g = _run_ragged(inp)
+    o = mqa_logits(inp.q, inp.kv, inp.kv_scale, inp.weights, inp.ks, inp.ke)
+    assert_logits_close(g, o, inp.ks, inp.ke, clean=True, what="tiny m64 n4096")
+
+
+def _random_windows(rng, m, n):
+    ks = rng.integers(0, n, m)
+    ke = np.minimum(n, ks + rng.integers(0, n, m))
+    # a few special windows: empty, full, single key, last key
+    ks[0], ke[0] = 0, n
+    if m > 1:
+        ks[1], ke[1] = 3 % n, 3 % n
+    if m > 2:
+        ks[2], ke[2] = n - 1, n
+    if m > 3:
+        ks[3], ke[3] = 0, 1
+    return ks.astype(np.int32), ke.astype(np.int32)
+
+
+@pytest.mark.parametrize("m,n", [(1, 17), (5, 64), (16, 65), (37, 1000), (50, 3000), (33, 4133)])
+@pytest.mark.parametrize("clean", [True, False])
+def test_ragged_shapes_and_windows(m, n, clean):
+    rng = np.random.default_rng(m * 1000 + n)
+    ks, ke = _random_windows(rng, m, n)
+    inp = ragged_inputs(m, n, 8, seed=m + n, ks=ks, ke=ke)
+    g = _run_ragged(inp, clean=clean)
+    o = mqa_logits(inp.q, inp.kv, inp.kv_scale, inp.weights, inp.ks, inp.ke)
+    assert_logits_close(g, o, inp.ks, inp.ke, clean=clean, what=f"m{m} n{n} clean{clean}")
+
+
+def test_ld_wider_than_n_leaves_tail_untouched():
+    inp = ragged_inputs(20, 700, 8, seed=3)
+    g = _run_ragged(inp, clean=True, ld=720)
+    o = mqa_logits(inp.q, inp.kv, inp.kv_scale, inp.weights, inp.ks, inp.ke)
+    assert_logits_close(g[:, :700], o, inp.ks, inp.ke, clean=True, what="ld 720")
+    assert np.all(g[:, 700:] == 12345.0)
+
+
+def test_multi_request_rows():
+    inp = multi_request_ragged([(300, 7), (1200, 20), (65, 3), (2048, 33)], k=16, seed=5)
+    g = _run_ragged(inp)
+    o = mqa_logits(inp.q, inp.kv, inp.kv_scale, inp.weights, inp.ks, inp.ke)
+    assert_logits_close(g, o, inp.ks, inp.ke, clean=True, what="multi-request")
+
+
+def test_signed_weights():
+    inp = ragged_inputs(24, 900, 8, seed=6, weight_mode="signed")
+    g = _run_ragged(inp)
+    o = mqa_logits(inp.q, inp.kv, inp.kv_scale, inp.weights, inp.ks, inp.ke)
+    extra = cancellation_tol(inp.q, inp.kv, inp.kv_scale, inp.weights, np.arange(24), 0, 900)
+    assert_logits_close(g, o, inp.ks, inp.ke, clean=True, extra_tol=extra, what="signed weights")
+
+
+@pytest.mark.parametrize("mode", ["zero_scale", "zero_weights"])
+def test_zero_scale_or_weights(mode):
+    kw = {"scale_mode": "zero"} if mode == "zero_scale" else {"weight_mode": "zero"}
+    inp = ragged_inputs(18, 300, 8, seed=7, **kw)
+    g = _run_ragged(inp)
+    inside = np.isfinite(mqa_logits(inp.q, inp.kv, inp.kv_scale, inp.weights, inp.ks, inp.ke))
+    assert np.all(g[inside] == 0.0)
+
+
+def test_extreme_codes_no_overflow():
+    # largest e4m3fn magnitudes: dot = 448*448*128 ~ 2.6e7 per head, well inside fp32
+    inp = ragged_inputs(4, 128, 8, seed=8)
+    inp.q[:] = 0x7E
+    inp.kv[:, :] = 0x7E
+    inp.kv[::2, ::2] = 0xFE
+    g = _run_ragged(inp)
+    o = mqa_logits(inp.q, inp.kv, inp.kv_scale, inp.weights, inp.ks, inp.ke)
+    assert_logits_close(g, o, inp.ks, inp.ke, clean=True, what="extreme codes")
+
+
+def test_rows_independent_of_batching():
+    # the value of (i, j) must not depend on which rows share a workgroup or key split
+    inp = ragged_inputs(40, 5000, 8, seed=9)
+    full = _run_ragged(inp)
+    rows = np.array([3, 17, 39])
+    q, kv, sc, w, ks, ke = _ragged_dev(inp)
+    sub = F.indexer_logits_ragged(q[rows], kv, sc, w[rows], ks[rows], ke[rows], clean=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(sub.cpu().numpy(), full[rows])
+
+
+# ---------------------------------------------------------------------------
+# paged decode
+# ---------------------------------------------------------------------------
+
+def _run_paged(inp, width, clean=True, block_table=None):
+    bt = inp.block_table if block_table is None else block_table
+    args = [to_dev(a) for a in (inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len, bt)]
+    g = F.indexer_logits_paged(*args, width=width, clean=clean)
+    torch.cuda.synchronize()
+    return g.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,next_n", [(3, 4), (2, 1), (2, 2), (3, 5), (1, 8)])
+def test_paged_vs_oracle(B, next_n):
+    inp = paged_inputs(B, next_n, 70, 2600, 16, seed=B * 10 + next_n, page_size=64)
+    width = int(inp.row_len.max())
+    g = _run_paged(inp, width)
+    o = paged_mqa_logits(inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len,
+                         inp.block_table, inp.page_size, width=width)
+    assert_logits_close(g, o, np.zeros(inp.rows, np.int64), inp.row_len, clean=True,
+                        what=f"paged B{B} next_n{next_n}")
+
+
+def test_paged_width_past_lengths_is_neg_inf():
+    inp = paged_inputs(2, 4, 500, 900, 16, seed=31, page_size=64)
+    width = inp.max_pages * 64
+    g = _run_paged(inp, width)
+    o = paged_mqa_logits(inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len,
+                         inp.block_table, inp.page_size, width=width)
+    assert_logits_close(g, o, np.zeros(inp.rows, np.int64), inp.row_len, clean=True, what="paged wide")
+
+
+def test_paged_invalid_page_ids_are_masked():
+    inp = paged_inputs(2, 4, 600, 700, 16, seed=32, page_size=64)
+    bt = inp.block_table.copy()
+    bt[0, 2] = -5                   # negative id
+    bt[1, 1] = inp.kv_pool.shape[0] + 3   # past the pool
+    width = int(inp.row_len.max())
+    g = _run_paged(inp, width, block_table=bt)
+    o = paged_mqa_logits(inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len,
+                         inp.block_table, inp.page_size, width=width)
+    for r in range(inp.rows):
+        b = r // 4
+        bad_page = 2 if b == 0 else 1
+        cols = np.arange(width)
+        masked = (cols // 64 == bad_page)
+        assert np.all(g[r, masked] == -np.inf)
+        keep = ~masked & (cols < inp.row_len[r])
+        d = np.abs(g[r, keep] - o[r, keep])
+        assert np.all(d <= 1e-3 + 2e-3 * np.abs(o[r, keep]))
+
+
+def test_paged_equals_ragged_on_gathered_kv():
+    inp = paged_inputs(2, 4, 900, 1500, 16, seed=33, page_size=64)
+    width = int(inp.row_len.max())
+    g = _run_paged(inp, width)
+    for b in range(inp.B):
+        n_b = int(inp.ctx[b])
+        pages = (n_b + 63) // 64
+        kv = inp.kv_pool[inp.block_table[b, :pages]].reshape(-1, D)[:n_b]
+        sc = inp.scale_pool[inp.block_table[b, :pages]].reshape(-1)[:n_b]
+        rows = slice(b * 4, b * 4 + 4)
+        q = inp.q[b]
+        gr = F.indexer_logits_ragged(to_dev(q), to_dev(kv), to_dev(sc), to_dev(inp.weights[rows]),
+                                     to_dev(np.zeros(4, np.int32)), to_dev(inp.row_len[rows]), clean=True)
+        torch.cuda.synchronize()
+        # same per-(row, key) arithmetic, so the two forms agree bit for bit
+        assert np.array_equal(gr.cpu().numpy(), g[rows, :n_b])
