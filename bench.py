@@ -1,0 +1,377 @@
+#!/usr/bin/env python3
+"""Benchmark of the fp8 MQA indexer hot path (logits + top-k) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = the whole hot path over one synthetic batch: the ragged fp8 MQA
+logits of every query row followed by the per-row top-k, i.e. exactly the two
+kernel launches the fused entry makes when its logits cap holds all rows
+(the chunking page's one-shot reference; its production cap of 8 GB also
+gives one chunk here).  Inputs are resident in HBM before timing starts.
+Rank 0 prints one JSON line.
+
+Extra modes (used to collect counters and cross-checks):
+  --fused-check        also time the fused C entry and report its ms/step
+  --no-cpu-baseline    skip the oracle timing (profiling runs)
+  --copy-calibration   only run a plain device copy of known size (for
+                       scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+  --all-workloads PATH time every workload and write a JSON list to PATH
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_FP8_PEAK = 5.0e15     # MI355X dense fp8 MFMA, FLOP/s
+HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+H, D = 32, 128
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+KERNEL_SOURCES = ["fp8_mqa_logits_amd/csrc/logits_ragged.hip", "fp8_mqa_logits_amd/csrc/mqa_core.hpp",
+                  "fp8_mqa_logits_amd/csrc/device_common.hpp", "fp8_mqa_logits_amd/csrc/logits_paged.hip",
+                  "fp8_mqa_logits_amd/csrc/topk.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_64k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--fused-check", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--all-workloads", default="")
+    return ap.parse_args()
+
+
+def _dev(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+# ---------------------------------------------------------------------------
+# ragged prefill workload
+# ---------------------------------------------------------------------------
+
+class RaggedStep:
+    def __init__(self, inp):
+        import torch
+        import fp8_mqa_logits_amd as F
+        self.F = F
+        self.inp = inp
+        self.q, self.kv, self.sc, self.w, self.ks, self.ke = (
+            _dev(inp.q), _dev(inp.kv), _dev(inp.kv_scale), _dev(inp.weights), _dev(inp.ks), _dev(inp.ke))
+        m, n, k = inp.m, inp.n, inp.k
+        self.cap = inp.cap_bytes
+        self.rpc = F.fp8idx_rows_per_chunk(self.cap, n, m)
+        self.ld = (n + 3) // 4 * 4
+        self.logits = torch.empty((self.rpc, self.ld), dtype=torch.float32, device="cuda")
+        tk = F.fp8idx_workspace_bytes(F.OP_TOPK, self.rpc, n, k, 0)
+        self.ws_topk = torch.empty(max(tk, 1) + 256, dtype=torch.uint8, device="cuda")
+        self.out = torch.empty((m, k), dtype=torch.int32, device="cuda")
+        fws = F.fp8idx_workspace_bytes(F.OP_LOGITS_TOPK_RAGGED, m, n, k, self.cap)
+        self.fused_ws = None
+        self.fused_ws_bytes = fws
+        self.events = []
+
+    def run(self, record=False):
+        """One pass of the hot path: per chunk, logits launch then top-k launch."""
+        import torch
+        F, inp = self.F, self.inp
+        for s in range(0, inp.m, self.rpc):
+            e = min(inp.m, s + self.rpc)
+            lg = self.logits[: e - s, : inp.n] if self.ld == inp.n else self.logits[: e - s]
+            if record:
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                ev[0].record()
+            F.indexer_logits_ragged(self.q[s:e], self.kv, self.sc, self.w[s:e], self.ks[s:e], self.ke[s:e],
+                                    clean=False, logits=self.logits[: e - s])
+            if record:
+                ev[1].record()
+            F.indexer_topk(self.logits[: e - s], self.ke[s:e], inp.k, ks=self.ks[s:e], width=inp.n, row0=s,
+                           out=self.out[s:e], workspace=self.ws_topk)
+            if record:
+                ev[2].record()
+                self.events.append((ev, e - s))
+
+    def run_fused(self):
+        import torch
+        if self.fused_ws is None:
+            self.fused_ws = torch.empty(self.fused_ws_bytes + 256, dtype=torch.uint8, device="cuda")
+        self.F.indexer_logits_topk_ragged(self.q, self.kv, self.sc, self.w, self.ks, self.ke, self.inp.k,
+                                          logits_cap_bytes=self.cap, out=self.out, workspace=self.fused_ws)
+
+    def kernel_times(self):
+        """Average logits and top-k launch durations (ms) over the recorded launches."""
+        lt = [ev[0].elapsed_time(ev[1]) for ev, _ in self.events]
+        tt = [ev[1].elapsed_time(ev[2]) for ev, _ in self.events]
+        return sum(lt) / len(lt), sum(tt) / len(tt), len(lt)
+
+    def flops(self):
+        return 2.0 * H * D * self.inp.valid_pairs
+
+    def topk_bytes(self):
+        # read each row's window once (fp32) and write k int32 indices per row
+        return 4.0 * self.inp.valid_pairs + 4.0 * self.inp.m * self.inp.k
+
+
+class PagedStep:
+    def __init__(self, inp):
+        import torch
+        import fp8_mqa_logits_amd as F
+        self.F = F
+        self.inp = inp
+        self.args = [_dev(a) for a in (inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len,
+                                       inp.block_table)]
+        self.width = inp.max_pages * 64
+        self.ld = (self.width + 3) // 4 * 4
+        self.logits = torch.empty((inp.rows, self.ld), dtype=torch.float32, device="cuda")
+        tk = F.fp8idx_workspace_bytes(F.OP_TOPK, inp.rows, self.width, inp.k, 0)
+        self.ws_topk = torch.empty(max(tk, 1) + 256, dtype=torch.uint8, device="cuda")
+        self.out = torch.empty((inp.rows, inp.k), dtype=torch.int32, device="cuda")
+        m = F.TopkMap(kind=F.MAP_BLOCK_TABLE, table=self.args[5], rows_per_req=inp.next_n, page_size=64)
+        self.map = m
+        self.fused_ws_bytes = F.fp8idx_workspace_bytes_paged(inp.B, inp.next_n, self.width, inp.k, 0)
+        self.fused_ws = None
+        self.events = []
+
+    def run(self, record=False):
+        import torch
+        F, inp = self.F, self.inp
+        if record:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record()
+        F.indexer_logits_paged(*self.args, width=self.width, clean=False, logits=self.logits)
+        if record:
+            ev[1].record()
+        F.indexer_topk(self.logits, self.args[4], inp.k, width=self.width, map=self.map, out=self.out,
+                       workspace=self.ws_topk)
+        if record:
+            ev[2].record()
+            self.events.append((ev, inp.rows))
+
+    def run_fused(self):
+        import torch
+        if self.fused_ws is None:
+            self.fused_ws = torch.empty(self.fused_ws_bytes + 256, dtype=torch.uint8, device="cuda")
+        self.F.indexer_logits_topk_paged(*self.args, self.inp.k, width=self.width, out=self.out,
+                                         workspace=self.fused_ws)
+
+    kernel_times = RaggedStep.kernel_times
+
+    def flops(self):
+        return 2.0 * H * D * self.inp.valid_pairs
+
+    def kv_bytes(self):
+        inp = self.inp
+        q = inp.rows * H * D
+        w = inp.rows * H * 4
+        bt = int(((inp.ctx.astype("int64") + 63) // 64).sum()) * 4
+        return float(inp.kv_bytes + q + w + bt + 4.0 * inp.valid_pairs)
+
+    def topk_bytes(self):
+        return 4.0 * self.inp.valid_pairs + 4.0 * self.inp.rows * self.inp.k
+
+
+def _time_steps(step, steps, warmup, record):
+    import torch
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    step.events = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step.run(record=record)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def _time_fused(step, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step.run_fused()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step.run_fused()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def _traffic(kernel_key):
+    """HBM bytes per launch from the committed counter runs, if they match these kernel sources."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    k = c.get("kernels", {}).get(kernel_key)
+    if not k:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def _cpu_baseline(inp, budget_s):
+    """Time the float64 oracle (logits + top-k) on an evenly spaced row sample."""
+    import numpy as np
+    from oracle import mqa_logits, topk_indices
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    order = np.linspace(0, inp.m - 1, num=min(inp.m, 512)).astype(np.int64)
+    done, valid, t_total = 0, 0, 0.0
+    block = 8
+    while done < order.size and (t_total < budget_s or done < 8):
+        rows = order[done:done + block]
+        t0 = time.perf_counter()
+        L = mqa_logits(inp.q[rows], inp.kv, inp.kv_scale, inp.weights[rows], inp.ks[rows], inp.ke[rows])
+        topk_indices(L, inp.ks[rows], inp.ke[rows], inp.k)
+        t_total += time.perf_counter() - t0
+        valid += int((inp.ke[rows].astype(np.int64) - inp.ks[rows]).clip(min=0).sum())
+        done += rows.size
+    tflops = 2.0 * H * D * valid / t_total / 1e12
+    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} evenly spaced rows of {inp.m} ({valid} valid (row, key) pairs), "
+                      f"float64 logits + top-k, {t_total:.1f} s; ms/layer-equivalent "
+                      f"{t_total * 1e3 * inp.valid_pairs / max(valid, 1):.0f}"}
+
+
+def run_workload(name, steps, warmup, fused_check):
+    import torch
+    from workloads.generate import config_inputs
+    inp = config_inputs(name)
+    paged = hasattr(inp, "kv_pool")
+    step = PagedStep(inp) if paged else RaggedStep(inp)
+    torch.cuda.synchronize()
+    ms = _time_steps(step, steps, warmup, record=True)
+    logit_ms, topk_ms, launches = step.kernel_times()
+    per_step = launches // steps
+    # per-launch averages times launches per step = kernel time per step (chunked workloads
+    # make one logits and one top-k launch per chunk)
+    res = {"workload": inp.name, "ms_per_step": ms, "logits_ms": logit_ms * per_step,
+           "topk_ms": topk_ms * per_step, "logits_ms_per_launch": logit_ms, "topk_ms_per_launch": topk_ms,
+           "launches_per_step": per_step, "flops": step.flops(), "inp": inp, "step": step}
+    if fused_check:
+        res["fused_ms_per_step"] = _time_fused(step, steps, warmup)
+    return res
+
+
+def copy_calibration():
+    import torch
+    nbytes = 1 << 30
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 3}), flush=True)
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}); "
+              "the indexer path is rank-local, see the sharding notes in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import fp8_mqa_logits_amd as F
+    F.load_library()
+    if a.copy_calibration:
+        copy_calibration()
+        return
+    if a.all_workloads:
+        rows = []
+        for name in ("tiny", "prefill_64k", "prefill_35k", "paged_decode", "long_prefix_210k"):
+            r = run_workload(name, a.steps, a.warmup, True)
+            inp, step = r.pop("inp"), r.pop("step")
+            r["logits_tflops"] = r["flops"] / (r["logits_ms"] * 1e-3) / 1e12
+            r["logits_mfma_frac"] = r["logits_tflops"] * 1e12 / MFMA_FP8_PEAK
+            r["topk_gbps"] = step.topk_bytes() / (r["topk_ms"] * 1e-3) / 1e9
+            if hasattr(step, "kv_bytes"):
+                r["logits_hbm_gbps"] = step.kv_bytes() / (r["logits_ms"] * 1e-3) / 1e9
+                r["logits_hbm_frac"] = r["logits_hbm_gbps"] * 1e9 / HBM_PEAK
+            rows.append(r)
+            print(json.dumps(r), file=sys.stderr, flush=True)
+            del inp, step
+            torch.cuda.empty_cache()
+        with open(a.all_workloads, "w") as f:
+            json.dump(rows, f, indent=1)
+        return
+
+    r = run_workload(a.workload, a.steps, a.warmup, a.fused_check)
+    inp, step = r["inp"], r["step"]
+    flops = r["flops"]
+    logit_tflops = flops / (r["logits_ms"] * 1e-3) / 1e12
+    paged = hasattr(inp, "kv_pool")
+    if paged:
+        achieved = step.kv_bytes() / (r["logits_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": _traffic("logits_paged")}
+        metric_value, unit = achieved, "GB/s"
+    else:
+        roof = {"bound": "mfma", "achieved": round(logit_tflops, 2), "peak": MFMA_FP8_PEAK / 1e12,
+                "unit": "TFLOP/s", "frac": round(logit_tflops * 1e12 / MFMA_FP8_PEAK, 4),
+                "traffic": _traffic("logits_ragged")}
+        metric_value, unit = flops / (r["ms_per_step"] * 1e-3) / 1e12, "TFLOP/s"
+    out = {
+        "metric": "indexer logits+top-k ms/layer & TFLOP/s (prefill), GB/s (decode), % roofline",
+        "value": round(metric_value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": inp.name},
+        "roofline": roof,
+        "logits_ms": round(r["logits_ms"], 4),
+        "topk_ms": round(r["topk_ms"], 4),
+        "topk_gbps": round(step.topk_bytes() / (r["topk_ms"] * 1e-3) / 1e9, 1),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if paged:
+        out["config"].update({"requests": inp.B, "rows_per_request": inp.next_n, "page_size": inp.page_size,
+                              "k": inp.k, "width": step.width, "valid_pairs": inp.valid_pairs})
+    else:
+        out["config"].update({"m": inp.m, "n": inp.n, "H": H, "D": D, "k": inp.k,
+                              "logits_cap_bytes": inp.cap_bytes, "rows_per_chunk": step.rpc,
+                              "valid_pairs": inp.valid_pairs})
+    if "fused_ms_per_step" in r:
+        out["fused_ms_per_step"] = round(r["fused_ms_per_step"], 4)
+    if not a.no_cpu_baseline and not paged:
+        out["cpu_baseline"] = _cpu_baseline(inp, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

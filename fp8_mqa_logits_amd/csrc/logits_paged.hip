@@ -12,11 +12,11 @@
 //   chunk lies past all of them, so the split of each request's keys over
 //   workgroups follows the device-side lengths without any host schedule.
 // - All 4 waves hold the same 4 query rows (q and weights in VGPRs) and take
-//   interleaved 16-key fragments of the chunk, loading each fragment's 16
-//   keys x 128 bytes (2 KiB, contiguous inside one page) straight from HBM
-//   into MFMA B-operands: every kv byte is read once and is shared by the 4
-//   query rows of the request.  Fragments are loaded kUnroll at a time so
-//   that several 2 KiB loads per wave are in flight.
+//   interleaved whole pages of the chunk: one wave-uniform page-id lookup per
+//   page, then the page's 64 keys x 128 bytes (8 KiB, contiguous) go straight
+//   from HBM into four MFMA B-operands.  Every kv byte is read once and is
+//   shared by the 4 query rows of the request; two pages per wave are in
+//   flight before any is scored.
 // - Scoring, ReLU, head weighting and the cross-lane head reduction are the
 //   same register-resident core as the ragged kernel.
 
@@ -29,7 +29,8 @@ namespace fp8idx {
 constexpr int kPage = 64;
 constexpr int kKeysPerWG = 1024;
 constexpr int kPagedWaves = 4;
-constexpr int kUnroll = 4;
+constexpr int kPagesInFlight = 2;                 // pages loaded ahead per wave
+constexpr int kFragsPerPage = kPage / 16;         // 16-key MFMA fragments per page
 
 __global__ __launch_bounds__(64 * kPagedWaves, 2) void logits_paged_kernel(PagedLogitsArgs a, int qgroups) {
   const int tid = threadIdx.x;
@@ -81,41 +82,55 @@ __global__ __launch_bounds__(64 * kPagedWaves, 2) void logits_paged_kernel(Paged
   const int32_t* __restrict__ bt = a.block_table + (int64_t)b * a.max_pages;
   const bool clean = a.clean != 0;
 
-  for (int f0 = wave; f0 < nfrag; f0 += kPagedWaves * kUnroll) {
-    v8i bfrag[kUnroll];
-    float sc[kUnroll];
-    bool pok[kUnroll];
+  // Wave w takes pages w, w + kPagedWaves, ... of the chunk, kPagesInFlight at a
+  // time: the page ids are read first (wave-uniform scalar loads), then every
+  // kv and scale load of those pages is issued, then the fragments are scored.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int first_page = c_lo / kPage;
+  const int npages = (covered - c_lo + kPage - 1) / kPage;
+  for (int pg0 = wave_u; pg0 < npages; pg0 += kPagedWaves * kPagesInFlight) {
+    int64_t page[kPagesInFlight];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int f = f0 + u * kPagedWaves;
-      const int j0 = c_lo + f * 16;
-      int64_t page = -1;
-      if (f < nfrag) page = bt[j0 / kPage];
-      pok[u] = page >= 0 && page < a.num_pages;
-      v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
-      float s = 0.f;
-      if (pok[u]) {
-        const int64_t slot = page * kPage + ((j0 + (lane & 15)) & (kPage - 1));
-        const v4i* p = reinterpret_cast<const v4i*>(a.kv_pool + slot * kDim + 32 * (lane >> 4));
-        const v4i x = p[0];
-        const v4i y = p[1];
-        v = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-        s = a.scale_pool[slot];
+    for (int u = 0; u < kPagesInFlight; ++u) {
+      const int pg = pg0 + u * kPagedWaves;
+      page[u] = pg < npages ? (int64_t)bt[first_page + pg] : -1;
+    }
+    v8i bfrag[kPagesInFlight][kFragsPerPage];
+    float sc[kPagesInFlight][kFragsPerPage];
+#pragma unroll
+    for (int u = 0; u < kPagesInFlight; ++u) {
+      const bool ok = page[u] >= 0 && page[u] < a.num_pages;
+      const int64_t pidx = ok ? page[u] : 0;
+#pragma unroll
+      for (int f = 0; f < kFragsPerPage; ++f) {
+        const int64_t slot = pidx * kPage + f * 16 + (lane & 15);
+        const v4i* ptr = reinterpret_cast<const v4i*>(a.kv_pool + slot * kDim + 32 * (lane >> 4));
+        v4i x = {0, 0, 0, 0}, y = {0, 0, 0, 0};
+        float s = 0.f;
+        if (ok) {
+          x = ptr[0];
+          y = ptr[1];
+          s = a.scale_pool[slot];
+        }
+        bfrag[u][f] = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        sc[u][f] = s;
       }
-      bfrag[u] = v;
-      sc[u] = s;
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int f = f0 + u * kPagedWaves;
-      if (f < nfrag) {
-        const float v = fragment_logit(qf, bfrag[u]) * sc[u];
-        const int j = c_lo + f * 16 + (lane & 15);
-        if (row_ok && j < c_hi) {
-          if (pok[u] && j < my_len) {
-            out_row[j] = v;
-          } else if (clean) {
-            out_row[j] = -INFINITY;
+    for (int u = 0; u < kPagesInFlight; ++u) {
+      const int pg = pg0 + u * kPagedWaves;
+      if (pg < npages) {
+        const bool ok = page[u] >= 0 && page[u] < a.num_pages;
+#pragma unroll
+        for (int f = 0; f < kFragsPerPage; ++f) {
+          const float v = fragment_logit(qf, bfrag[u][f]) * sc[u][f];
+          const int j = c_lo + pg * kPage + f * 16 + (lane & 15);
+          if (row_ok && j < covered) {
+            if (ok && j < my_len) {
+              out_row[j] = v;
+            } else if (clean) {
+              out_row[j] = -INFINITY;
+            }
           }
         }
       }

@@ -12,16 +12,22 @@
 //   sort like the floats (-0.0 folded onto +0.0; key 0 marks padding).
 //   Wave w holds positions [w * 64 * VPT, (w + 1) * 64 * VPT), so
 //   (wave, register, lane) order is position order.
-// - The segment's min and max key fix the bits all keys share; the remaining
-//   bits are resolved 11 at a time, most significant first: an LDS histogram
-//   of the current digit over the keys that still match the prefix, then a
-//   suffix scan finds the digit holding the k-th largest key.  After at most
-//   three passes the exact threshold key tau is known, with the number of
-//   elements equal to tau that still need to be taken.
-// - Emission: elements above tau, plus the lowest-positioned elements equal
-//   to tau, get output slots from wave ballots and a cross-wave prefix sum,
-//   so outputs are written in ascending position order and the result is
-//   deterministic.
+// - Candidate threshold: one key register in 16 forms a strided sample; the
+//   sample key of rank ~1.25 * k * (sample / segment) + 16 becomes a lower
+//   threshold T.  A popcount pass counts the keys >= T; when they number at
+//   least k (and fit the LDS list) a second pass compacts them into LDS in
+//   position order, using wave ballots and per-wave offsets.  Segments that
+//   fit the list whole skip the sample (T = every key).
+// - Exact selection on the candidates: the bits shared by T and the maximum
+//   are fixed; the rest are resolved 11 at a time, most significant first,
+//   with an LDS histogram and a suffix scan per digit.  This yields the exact
+//   k-th key tau and the number of elements equal to tau still to take.
+// - Emission: each thread walks a contiguous run of the ordered candidates;
+//   an exclusive scan over threads gives output slots, so elements above
+//   tau plus the lowest-positioned elements equal to tau are written in
+//   ascending position order and the output is deterministic.
+// - If the sample misjudges (fewer than k candidates, or too many for LDS),
+//   the same exact selection runs over every key in registers instead.
 // - Rows longer than one segment are split: each segment emits its local
 //   top-k (key, index) candidates in position order, and further levels of
 //   the same kernel select from the concatenated candidates.  Because the
@@ -62,6 +68,8 @@ struct TopkKernelArgs {
 
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
+constexpr int kCandCap = 8192;      // capacity of the LDS candidate list
+constexpr int kSampleStride = 16;   // one key register in 16 feeds the threshold sample
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
@@ -115,18 +123,174 @@ __device__ __forceinline__ int map_request(const TopkMap& m, int grow) {
   return 0;
 }
 
+// LDS of one workgroup: digit histogram, the ordered candidate list and
+// small per-wave scratch for reductions and scans.
+template <int NW>
+struct TopkShared {
+  uint32_t hist[kBins];
+  uint32_t ck[kCandCap];   // candidate keys, in position order
+  uint32_t cp[kCandCap];   // candidate positions within the segment
+  uint32_t w0[NW];
+  uint32_t w1[NW];
+  uint32_t w2[NW];
+  uint32_t digit;
+  uint32_t above;
+};
+
+// Exact rank-th largest key (1 <= rank <= count) of a multiset of keys spread
+// over the workgroup, all inside [lo, hi].  for_each(visit) calls visit(key)
+// on each of the calling thread's keys.  On return `need` holds how many
+// elements equal to the result belong to the rank largest.  The bits shared
+// by lo and hi are fixed up front; the rest are resolved 11 at a time, most
+// significant first, with an LDS histogram and a suffix scan per digit.
+template <int THREADS, typename ForEach>
+__device__ uint32_t radix_select(ForEach for_each, uint32_t lo, uint32_t hi, uint32_t rank, uint32_t& need,
+                                 TopkShared<THREADS / 64>& sh) {
+  constexpr int NW = THREADS / 64;
+  constexpr int DPT = kBins / THREADS;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  need = rank;
+  if (lo == hi) return hi;
+  const int hb = 31 - __builtin_clz(lo ^ hi);
+  uint32_t pmask = hb == 31 ? 0u : ~((2u << hb) - 1u);
+  uint32_t prefix = hi & pmask;
+  int top = hb;
+  while (top >= 0) {
+    const int shift = max(0, top - (kDigitBits - 1));
+    const uint32_t dmask = (2u << (top - shift)) - 1u;
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) sh.hist[tid * DPT + i] = 0u;
+    __syncthreads();
+    for_each([&](uint32_t v) {
+      if ((v & pmask) == prefix) atomicAdd(&sh.hist[(v >> shift) & dmask], 1u);
+    });
+    __syncthreads();
+    uint32_t mine[DPT];
+    uint32_t st = 0u;
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) {
+      mine[i] = sh.hist[tid * DPT + i];
+      st += mine[i];
+    }
+    uint32_t incl = st;   // suffix sum over this and higher lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t v = (uint32_t)__shfl_down((int)incl, o);
+      if (lane + o < 64) incl += v;
+    }
+    if (lane == 0) sh.w0[wave] = incl;
+    __syncthreads();
+    uint32_t above = incl - st;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (w > wave) above += sh.w0[w];
+    if (above < need && need <= above + st) {
+      uint32_t acc = above;
+#pragma unroll
+      for (int i = DPT - 1; i >= 0; --i) {
+        if (acc < need && acc + mine[i] >= need) {
+          sh.digit = (uint32_t)(tid * DPT + i);
+          sh.above = acc;
+        }
+        acc += mine[i];
+      }
+    }
+    __syncthreads();
+    need -= sh.above;
+    prefix |= sh.digit << shift;
+    pmask |= dmask << shift;
+    top = shift - 1;
+  }
+  return prefix;
+}
+
+// Block-wide reduction of (max, min, sum) over the workgroup.
+template <int NW>
+__device__ void block_max_min_sum(uint32_t& mx, uint32_t& mn, uint32_t& sm, TopkShared<NW>& sh) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  mx = wave_max_u32(mx);
+  mn = wave_min_u32(mn);
+  sm = wave_sum_u32(sm);
+  __syncthreads();   // earlier readers of w0..w2 are done
+  if (lane == 0) {
+    sh.w0[wave] = mx;
+    sh.w1[wave] = mn;
+    sh.w2[wave] = sm;
+  }
+  __syncthreads();
+  mx = 0u;
+  mn = 0xffffffffu;
+  sm = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    mx = max(mx, sh.w0[w]);
+    mn = min(mn, sh.w1[w]);
+    sm += sh.w2[w];
+  }
+}
+
+// Exclusive prefix sums over threads (thread order) of two per-thread counts.
+template <int NW>
+__device__ void block_excl_scan2(uint32_t a, uint32_t b, uint32_t& a_before, uint32_t& b_before,
+                                 TopkShared<NW>& sh) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint32_t ia = a, ib = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t ta = (uint32_t)__shfl_up((int)ia, o);
+    const uint32_t tb = (uint32_t)__shfl_up((int)ib, o);
+    if (lane >= o) {
+      ia += ta;
+      ib += tb;
+    }
+  }
+  __syncthreads();
+  if (lane == 63) {
+    sh.w0[wave] = ia;
+    sh.w1[wave] = ib;
+  }
+  __syncthreads();
+  a_before = ia - a;
+  b_before = ib - b;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) {
+      a_before += sh.w0[w];
+      b_before += sh.w1[w];
+    }
+  }
+}
+
+template <bool LEVEL0, bool FINAL>
+struct Emitter {
+  const TopkKernelArgs& a;
+  int64_t sa;
+  int64_t row;
+  int64_t out_base;
+  int req;
+  int row_ks;
+  __device__ __forceinline__ void operator()(uint32_t o, uint32_t pos, uint32_t key) const {
+    int32_t j;
+    if (LEVEL0) j = (int32_t)(sa + pos);
+    else j = a.in_idx[row * a.in_len + sa + pos];
+    if (FINAL) {
+      a.out[out_base + o] = map_index(a.map, req, row_ks, j);
+    } else {
+      a.out_keys[out_base + o] = key;
+      a.out_idx[out_base + o] = j;
+    }
+  }
+};
+
 template <int THREADS, int VPT, bool LEVEL0, bool FINAL>
 __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
   constexpr int NW = THREADS / 64;
-  constexpr int DPT = kBins / THREADS;   // histogram bins per thread
   static_assert(kBins % THREADS == 0, "bins per thread");
-
-  __shared__ uint32_t s_hist[kBins];
-  __shared__ uint32_t s_w0[NW];
-  __shared__ uint32_t s_w1[NW];
-  __shared__ uint32_t s_w2[NW];
-  __shared__ uint32_t s_digit;
-  __shared__ uint32_t s_above;
+  __shared__ TopkShared<NW> sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -136,8 +300,8 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
 
   // ---- segment window -------------------------------------------------------
   int row_ks = 0;
-  int64_t sa;
-  int len;
+  int64_t sa = 0;
+  int len = 0;
   if (LEVEL0 || FINAL) {
     const int e = min(max(a.ke[row], 0), a.width);
     row_ks = a.ks ? min(max(a.ks[row], 0), e) : 0;
@@ -151,31 +315,32 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
     len = (int)max((int64_t)0, min((int64_t)a.seg_len, a.in_len - sa));
   }
 
-  // ---- load keys --------------------------------------------------------------
+  // ---- load keys into VGPRs -------------------------------------------------
+  // Loads are unconditional from a clamped in-bounds position (len >= 1);
+  // positions past the segment are then replaced by the padding key 0.
   uint32_t key[VPT];
   const int base = wave * (64 * VPT) + lane;
-  // Loads are unconditional from a clamped in-bounds position (len >= 1);
-  // positions past the segment are then replaced by the padding key.
   const int last = max(len - 1, 0);
   if (len == 0) {
 #pragma unroll
     for (int p = 0; p < VPT; ++p) key[p] = 0u;
   } else if (LEVEL0) {
     const float* src = a.logits + (int64_t)row * a.ld + sa;
+    // all VPT loads are issued before any is consumed: the padding mask is
+    // applied arithmetically so no load sits under a branch
+#pragma unroll
+    for (int p = 0; p < VPT; ++p) key[p] = __float_as_uint(__builtin_nontemporal_load(src + min(base + p * 64, last)));
 #pragma unroll
     for (int p = 0; p < VPT; ++p) {
-      const int pos = base + p * 64;
-      const float x = __builtin_nontemporal_load(src + min(pos, last));
-      key[p] = pos < len ? max(float_to_ordered(x), 1u) : 0u;
+      const uint32_t keep = 0u - (uint32_t)(base + p * 64 < len);
+      key[p] = max(float_to_ordered(__uint_as_float(key[p])), 1u) & keep;
     }
   } else {
     const uint32_t* src = a.in_keys + (int64_t)row * a.in_len + sa;
 #pragma unroll
-    for (int p = 0; p < VPT; ++p) {
-      const int pos = base + p * 64;
-      const uint32_t x = src[min(pos, last)];
-      key[p] = pos < len ? x : 0u;
-    }
+    for (int p = 0; p < VPT; ++p) key[p] = src[min(base + p * 64, last)];
+#pragma unroll
+    for (int p = 0; p < VPT; ++p) key[p] &= 0u - (uint32_t)(base + p * 64 < len);
   }
 
   // ---- valid count, min and max ---------------------------------------------
@@ -189,139 +354,149 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
       ++cnt;
     }
   }
-  kmax = wave_max_u32(kmax);
-  kmin = wave_min_u32(kmin);
-  cnt = wave_sum_u32(cnt);
-  if (lane == 0) {
-    s_w0[wave] = kmax;
-    s_w1[wave] = kmin;
-    s_w2[wave] = cnt;
-  }
-  __syncthreads();
-  kmax = 0u;
-  kmin = 0xffffffffu;
-  cnt = 0u;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    kmax = max(kmax, s_w0[w]);
-    kmin = min(kmin, s_w1[w]);
-    cnt += s_w2[w];
-  }
+  block_max_min_sum<NW>(kmax, kmin, cnt, sh);
   const uint32_t kk = min((uint32_t)a.k, cnt);
 
-  int req = 0;
-  if (FINAL) req = map_request(a.map, a.row0 + row);
+  const int64_t out_base = FINAL ? (int64_t)row * a.ld_out : ((int64_t)row * a.nseg + seg) * (int64_t)a.k;
+  Emitter<LEVEL0, FINAL> emit{a, sa, row, out_base, FINAL ? map_request(a.map, a.row0 + row) : 0, row_ks};
 
-  // ---- threshold --------------------------------------------------------------
-  uint32_t tau = kmax;
-  uint32_t need = kk;   // elements equal to tau still to take, once tau is final
-  if (kk > 0u && kmin != kmax) {
-    const int hb = 31 - __builtin_clz(kmin ^ kmax);   // highest differing bit
-    uint32_t prefix = kmax & ~((2u << hb) - 1u);
-    uint32_t pmask = ~((2u << hb) - 1u);
-    if (hb == 31) { prefix = 0u; pmask = 0u; }
-    int top = hb;
-    while (top >= 0) {
-      const int shift = max(0, top - (kDigitBits - 1));
-      const uint32_t dmask = (2u << (top - shift)) - 1u;
+  if (kk > 0u) {
+    // ---- candidate threshold T from a strided sample ---------------------------
+    // Target: about 1.25 * kk + 16 sample-strides of elements at or above T, so
+    // that the exact k-th key is almost always among the candidates.
+    uint32_t T = 1u;   // 1 = every valid key
+    if (cnt > (uint32_t)kCandCap) {
+      uint32_t smax = 0u, smin = 0xffffffffu, ns = 0u;
 #pragma unroll
-      for (int i = 0; i < DPT; ++i) s_hist[tid * DPT + i] = 0u;
+      for (int p = 0; p < VPT; p += kSampleStride) {
+        const uint32_t v = key[p];
+        if (v != 0u) {
+          smax = max(smax, v);
+          smin = min(smin, v);
+          ++ns;
+        }
+      }
+      block_max_min_sum<NW>(smax, smin, ns, sh);
+      const uint64_t want = ((uint64_t)kk * ns * 5u + 4ull * cnt - 1u) / (4ull * cnt) + 16u;
+      if (ns > 0u && want < ns) {
+        uint32_t unused;
+        T = radix_select<THREADS>(
+            [&](auto&& visit) {
+#pragma unroll
+              for (int p = 0; p < VPT; p += kSampleStride)
+                if (key[p] != 0u) visit(key[p]);
+            },
+            smin, smax, (uint32_t)want, unused, sh);
+      }
+    }
+
+    // ---- count candidates (keys >= T) per wave --------------------------------
+    uint32_t cw = 0u;
+#pragma unroll
+    for (int p = 0; p < VPT; ++p) cw += (uint32_t)__popcll(ballot64(key[p] >= T));
+    __syncthreads();
+    if (lane == 0) sh.w2[wave] = cw;
+    __syncthreads();
+    uint32_t C = 0u, woff = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t x = sh.w2[w];
+      if (w < wave) woff += x;
+      C += x;
+    }
+
+    if (C >= kk && C <= (uint32_t)kCandCap) {
+      // ---- ordered compaction of the candidates into LDS -----------------------
+      uint32_t off = woff;
+#pragma unroll
+      for (int p = 0; p < VPT; ++p) {
+        const bool c = key[p] >= T;
+        const uint64_t b = ballot64(c);
+        if (c) {
+          const uint32_t o = off + mbcnt64(b);
+          sh.ck[o] = key[p];
+          sh.cp[o] = (uint32_t)(base + p * 64);
+        }
+        off += (uint32_t)__popcll(b);
+      }
       __syncthreads();
+      // ---- exact threshold among the candidates --------------------------------
+      uint32_t need;
+      const uint32_t tau = radix_select<THREADS>(
+          [&](auto&& visit) {
+            for (uint32_t i = tid; i < C; i += THREADS) visit(sh.ck[i]);
+          },
+          T, kmax, kk, need, sh);
+      // ---- emission in position order ------------------------------------------
+      const uint32_t per = (C + THREADS - 1) / THREADS;
+      const uint32_t c0 = min(C, (uint32_t)tid * per);
+      const uint32_t c1 = min(C, c0 + per);
+      uint32_t gt = 0u, eq = 0u;
+      for (uint32_t i = c0; i < c1; ++i) {
+        const uint32_t v = sh.ck[i];
+        gt += v > tau;
+        eq += v == tau;
+      }
+      uint32_t gt_before, eq_before;
+      block_excl_scan2<NW>(gt, eq, gt_before, eq_before, sh);
+      uint32_t run_eq = eq_before;
+      uint32_t run_sel = gt_before + min(eq_before, need);
+      for (uint32_t i = c0; i < c1; ++i) {
+        const uint32_t v = sh.ck[i];
+        bool sel = v > tau;
+        if (v == tau) {
+          sel = run_eq < need;
+          ++run_eq;
+        }
+        if (sel) {
+          emit(run_sel, sh.cp[i], v);
+          ++run_sel;
+        }
+      }
+    } else {
+      // ---- fallback: exact select over every key in registers -------------------
+      uint32_t need;
+      const uint32_t tau = radix_select<THREADS>(
+          [&](auto&& visit) {
+#pragma unroll
+            for (int p = 0; p < VPT; ++p)
+              if (key[p] != 0u) visit(key[p]);
+          },
+          kmin, kmax, kk, need, sh);
+      uint32_t gt = 0u, eq = 0u;
+#pragma unroll
+      for (int p = 0; p < VPT; ++p) {
+        gt += (uint32_t)__popcll(ballot64(key[p] > tau));
+        eq += (uint32_t)__popcll(ballot64(key[p] == tau));
+      }
+      __syncthreads();
+      if (lane == 0) {
+        sh.w0[wave] = gt;
+        sh.w1[wave] = eq;
+      }
+      __syncthreads();
+      uint32_t gt_before = 0u, eq_before = 0u;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        if (w < wave) {
+          gt_before += sh.w0[w];
+          eq_before += sh.w1[w];
+        }
+      }
+      uint32_t run_eq = eq_before;
+      uint32_t run_sel = gt_before + min(eq_before, need);
 #pragma unroll
       for (int p = 0; p < VPT; ++p) {
         const uint32_t v = key[p];
-        if (v != 0u && (v & pmask) == prefix) atomicAdd(&s_hist[(v >> shift) & dmask], 1u);
+        const bool is_gt = v > tau;
+        const bool is_eq = v == tau;
+        const uint64_t beq = ballot64(is_eq);
+        const bool sel = is_gt || (is_eq && (run_eq + mbcnt64(beq)) < need);
+        const uint64_t bsel = ballot64(sel);
+        if (sel) emit(run_sel + mbcnt64(bsel), (uint32_t)(base + p * 64), v);
+        run_eq += (uint32_t)__popcll(beq);
+        run_sel += (uint32_t)__popcll(bsel);
       }
-      __syncthreads();
-      uint32_t mine[DPT];
-      uint32_t st = 0u;
-#pragma unroll
-      for (int i = 0; i < DPT; ++i) {
-        mine[i] = s_hist[tid * DPT + i];
-        st += mine[i];
-      }
-      uint32_t incl = st;   // inclusive suffix sum over lanes >= this lane
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = (uint32_t)__shfl_down((int)incl, o);
-        if (lane + o < 64) incl += v;
-      }
-      if (lane == 0) s_w0[wave] = incl;
-      __syncthreads();
-      uint32_t above = incl - st;
-#pragma unroll
-      for (int w = 0; w < NW; ++w)
-        if (w > wave) above += s_w0[w];
-      if (above < need && need <= above + st) {
-        uint32_t acc = above;
-#pragma unroll
-        for (int i = DPT - 1; i >= 0; --i) {
-          if (acc + mine[i] >= need && acc < need) {
-            s_digit = (uint32_t)(tid * DPT + i);
-            s_above = acc;
-          }
-          acc += mine[i];
-        }
-      }
-      __syncthreads();
-      const uint32_t d = s_digit;
-      need -= s_above;
-      prefix |= d << shift;
-      pmask |= dmask << shift;
-      top = shift - 1;
-    }
-    tau = prefix;
-  }
-
-  // ---- emission ---------------------------------------------------------------
-  const int64_t out_base = FINAL ? (int64_t)row * a.ld_out
-                                 : ((int64_t)row * a.nseg + seg) * (int64_t)a.k;
-  if (kk > 0u) {
-    uint32_t gt = 0u, eq = 0u;
-#pragma unroll
-    for (int p = 0; p < VPT; ++p) {
-      gt += (uint32_t)__popcll(ballot64(key[p] > tau));
-      eq += (uint32_t)__popcll(ballot64(key[p] == tau));
-    }
-    __syncthreads();   // s_w0 reuse
-    if (lane == 0) {
-      s_w0[wave] = gt;
-      s_w1[wave] = eq;
-    }
-    __syncthreads();
-    uint32_t gt_before = 0u, eq_before = 0u;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      if (w < wave) {
-        gt_before += s_w0[w];
-        eq_before += s_w1[w];
-      }
-    }
-    uint32_t run_eq = eq_before;
-    uint32_t run_sel = gt_before + min(eq_before, need);
-#pragma unroll
-    for (int p = 0; p < VPT; ++p) {
-      const uint32_t v = key[p];
-      const bool is_gt = v > tau;
-      const bool is_eq = v == tau;
-      const uint64_t beq = ballot64(is_eq);
-      const bool sel = is_gt || (is_eq && (run_eq + mbcnt64(beq)) < need);
-      const uint64_t bsel = ballot64(sel);
-      if (sel) {
-        const uint32_t o = run_sel + mbcnt64(bsel);
-        const int pos = base + p * 64;
-        int32_t j;
-        if (LEVEL0) j = (int32_t)(sa + pos);
-        else j = a.in_idx[(int64_t)row * a.in_len + sa + pos];
-        if (FINAL) {
-          a.out[out_base + o] = map_index(a.map, req, row_ks, j);
-        } else {
-          a.out_keys[out_base + o] = v;
-          a.out_idx[out_base + o] = j;
-        }
-      }
-      run_eq += (uint32_t)__popcll(beq);
-      run_sel += (uint32_t)__popcll(bsel);
     }
   }
   // padding after the kk selected entries
