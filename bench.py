@@ -241,7 +241,7 @@ def _cpu_baseline(inp, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    order = np.linspace(0, inp.m - 1, num=min(inp.m, 512)).astype(np.int64)
+    order = np.linspace(0, inp.m - 1, num=min(inp.m, 4096)).astype(np.int64)
     done, valid, t_total = 0, 0, 0.0
     block = 8
     while done < order.size and (t_total < budget_s or done < 8):

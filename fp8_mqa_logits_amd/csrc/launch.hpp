@@ -85,7 +85,11 @@ struct TopkPlan {
 // Device properties the launchers need, cached per device.
 struct DeviceInfo {
   int cu_count;
+  int ragged_wgs_per_cu;   // resident workgroups of the ragged logits kernel per CU
 };
+
+// Fills the occupancy fields of `d` (called once per device).
+void query_ragged_occupancy(DeviceInfo& d);
 
 TopkPlan plan_topk(int32_t rows, int64_t width, int32_t k);
 size_t topk_workspace_bytes(const TopkPlan& p);

@@ -31,6 +31,12 @@ __device__ __forceinline__ v4f load_w4(const float* __restrict__ w, int row, boo
   return r;
 }
 
+// ReLU as one integer max on the float's bits: a set sign bit makes the
+// int32 negative, so negative values (and -0.0) become +0.0 and non-negative
+// values pass unchanged.  fmaxf would first canonicalise its input (NaN
+// quieting), costing a second VALU op per score.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Scores of the wave's 4 rows against one 16-key B fragment, reduced over heads.
 // Returns the unscaled logit of (row qsel(lane), key lane % 16).
 __device__ __forceinline__ float fragment_logit(const QFrags& f, const v8i& b) {
@@ -40,14 +46,14 @@ __device__ __forceinline__ float fragment_logit(const QFrags& f, const v8i& b) {
   for (int qi = 0; qi < 4; ++qi) {
     const v4f s0 = mfma_fp8_16x16x128(f.a[qi][0], b, zero);
     const v4f s1 = mfma_fp8_16x16x128(f.a[qi][1], b, zero);
-    float acc = f.w[qi][0][0] * fmaxf(s0[0], 0.f);
-    acc = fmaf(f.w[qi][0][1], fmaxf(s0[1], 0.f), acc);
-    acc = fmaf(f.w[qi][0][2], fmaxf(s0[2], 0.f), acc);
-    acc = fmaf(f.w[qi][0][3], fmaxf(s0[3], 0.f), acc);
-    acc = fmaf(f.w[qi][1][0], fmaxf(s1[0], 0.f), acc);
-    acc = fmaf(f.w[qi][1][1], fmaxf(s1[1], 0.f), acc);
-    acc = fmaf(f.w[qi][1][2], fmaxf(s1[2], 0.f), acc);
-    acc = fmaf(f.w[qi][1][3], fmaxf(s1[3], 0.f), acc);
+    float acc = f.w[qi][0][0] * relu_bits(s0[0]);
+    acc = fmaf(f.w[qi][0][1], relu_bits(s0[1]), acc);
+    acc = fmaf(f.w[qi][0][2], relu_bits(s0[2]), acc);
+    acc = fmaf(f.w[qi][0][3], relu_bits(s0[3]), acc);
+    acc = fmaf(f.w[qi][1][0], relu_bits(s1[0]), acc);
+    acc = fmaf(f.w[qi][1][1], relu_bits(s1[1]), acc);
+    acc = fmaf(f.w[qi][1][2], relu_bits(s1[2]), acc);
+    acc = fmaf(f.w[qi][1][3], relu_bits(s1[3]), acc);
     p[qi] = acc;
   }
   return reduce_rows4(p[0], p[1], p[2], p[3]);
