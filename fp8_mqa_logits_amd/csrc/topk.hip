@@ -5,37 +5,47 @@
 //
 // Selection rule: the k largest logits of the row's window [ks, ke), ties at
 // the k-th value going to the lower key index, so the selected set is unique.
+// Keys are compared as order-preserving uint32 codes of the floats (-0.0 is
+// folded onto +0.0; code 0 marks padding).
 //
-// Algorithm (exact radix select on order-preserving keys):
-// - Each workgroup owns one segment of one row: up to THREADS * VPT elements,
-//   loaded once with coalesced loads and kept in VGPRs as uint32 keys that
-//   sort like the floats (-0.0 folded onto +0.0; key 0 marks padding).
-//   Wave w holds positions [w * 64 * VPT, (w + 1) * 64 * VPT), so
-//   (wave, register, lane) order is position order.
-// - Candidate threshold: one key register in 16 forms a strided sample; the
-//   sample key of rank ~1.25 * k * (sample / segment) + 16 becomes a lower
-//   threshold T.  A popcount pass counts the keys >= T; when they number at
-//   least k (and fit the LDS list) a second pass compacts them into LDS in
-//   position order, using wave ballots and per-wave offsets.  Segments that
-//   fit the list whole skip the sample (T = every key).
-// - Exact selection on the candidates: the bits shared by T and the maximum
-//   are fixed; the rest are resolved 11 at a time, most significant first,
-//   with an LDS histogram and a suffix scan per digit.  This yields the exact
-//   k-th key tau and the number of elements equal to tau still to take.
-// - Emission: each thread walks a contiguous run of the ordered candidates;
-//   an exclusive scan over threads gives output slots, so elements above
-//   tau plus the lowest-positioned elements equal to tau are written in
-//   ascending position order and the output is deterministic.
-// - If the sample misjudges (fewer than k candidates, or too many for LDS),
-//   the same exact selection runs over every key in registers instead.
-// - Rows longer than one segment are split: each segment emits its local
-//   top-k (key, index) candidates in position order, and further levels of
-//   the same kernel select from the concatenated candidates.  Because the
-//   rule is a total order (value desc, index asc), a row's top-k is always
-//   contained in the union of its segments' top-k.
-// - The last level maps each selected key index through the token table
-//   (page size 1: table[req(i), j - ks[i]]) or the block table
-//   (table[b, j / page] * page + j % page), or writes j itself.
+// Algorithm: one workgroup of 256 threads per (row, segment of at most 65536
+// keys), streaming the segment from memory; nothing is held per key in
+// registers, so several workgroups share a CU and their loads overlap each
+// other's selection work.
+// 1. Threshold: 16 runs of 256 consecutive keys, spread evenly over the
+//    segment, form a sample; a radix search over the sample, stopped once
+//    the bin in question holds at most 16 sample keys, gives a lower
+//    threshold T near the sample rank 1.3 * k * (sample / segment) + 16 (a
+//    segment that fits the LDS candidate list whole takes every key).
+// 2. Compaction: one streaming pass with 16-byte loads appends every key >= T
+//    (about 1.3 k of them) as a (code, position) pair to an LDS list; each
+//    wave claims its slots with one LDS atomic per 32 keys a lane examined,
+//    while the next 32 keys per lane are already loading.  The list order
+//    depends on timing.
+// 3. Boundary bin: a 2048-bin histogram of the list between T and the sample
+//    maximum locates the bin of the k-th largest code; every candidate in a
+//    higher bin is selected, and the few in that bin are ranked pairwise by
+//    (value desc, position asc), which settles the k-th value and its ties
+//    in one step.  (If that bin holds more than 256 candidates, e.g. under
+//    heavy ties, an exact radix search over the list finds the k-th code
+//    tau, and the ties at tau are ranked by position through an LDS bitmap
+//    with per-word prefix popcounts.)
+// 4. Order: the positions of the selected keys are set in an LDS bitmap, and
+//    each key's output slot is its rank by position (prefix popcount).  The
+//    output row is the selected keys in ascending position order, identical
+//    on every run.
+// If the sample misjudges (fewer than k candidates, or more than fit), the
+// same exact selection and ordering run over every key of the segment,
+// streamed from memory once per step.
+// Rows longer than one segment, or few rows that need more parallelism, are
+// split: each segment emits its local top-k (code, index) pairs in index
+// order, and further levels of the same kernel select from the concatenated
+// pairs (still in index order, so position order is index order).  Because
+// the rule is a total order (value desc, index asc), a row's top-k is always
+// contained in the union of its segments' top-k.  The last level maps each
+// selected key index through the token table (page size 1:
+// table[req(i), j - ks[i]]) or the block table (table[b, j / page] * page +
+// j % page), or writes j itself.
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -68,8 +78,20 @@ struct TopkKernelArgs {
 
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
-constexpr int kCandCap = 8192;      // capacity of the LDS candidate list
-constexpr int kSampleStride = 16;   // one key register in 16 feeds the threshold sample
+constexpr int64_t kMaxSeg = 65536;                                // keys per segment
+constexpr int kBitmapWords = (int)((kMaxSeg + 4 + 31) / 32) + 1;  // positions from the 16-byte load base
+constexpr int kTopkThreads = 256;
+constexpr int kSampleRuns = 16;
+constexpr int kSampleSize = kSampleRuns * kTopkThreads;
+constexpr int kElemsPerPass = 32;   // keys a thread loads per streaming pass
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+constexpr int kBoundaryMax = kTopkThreads;   // boundary-bin candidates ranked pairwise
+
+// Candidate-list capacity for k: the expected list (1.3 k + 24 sample units
+// of keys, at most 384 keys) must stay under 7/8 of it.
+constexpr int kSmallCap = 4096;
+constexpr int kBigCap = 16384;
+inline bool topk_needs_big_cap(int64_t k) { return k * 13 / 10 + 512 > (int64_t)kSmallCap * 7 / 8; }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
@@ -123,34 +145,85 @@ __device__ __forceinline__ int map_request(const TopkMap& m, int grow) {
   return 0;
 }
 
-// LDS of one workgroup: digit histogram, the ordered candidate list and
-// small per-wave scratch for reductions and scans.
-template <int NW>
+// LDS of one workgroup.
+template <int NW, int CAP>
 struct TopkShared {
-  uint32_t hist[kBins];
-  uint32_t ck[kCandCap];   // candidate keys, in position order
-  uint32_t cp[kCandCap];   // candidate positions within the segment
+  v2u cand[CAP];                    // candidates (code, position); bitmaps in the fallback
+  uint32_t hist[kBitmapWords];      // digit histogram, later per-word prefix popcounts
+  uint32_t bits[kBitmapWords];      // position bitmap
+  uint32_t bk[kBoundaryMax];        // codes of the candidates in the boundary bin
+  uint32_t bp[kBoundaryMax];        // and their positions
   uint32_t w0[NW];
   uint32_t w1[NW];
   uint32_t w2[NW];
+  uint32_t cnt;
+  uint32_t nb;
   uint32_t digit;
   uint32_t above;
+  uint32_t dcount;
 };
 
-// Exact rank-th largest key (1 <= rank <= count) of a multiset of keys spread
-// over the workgroup, all inside [lo, hi].  for_each(visit) calls visit(key)
-// on each of the calling thread's keys.  On return `need` holds how many
-// elements equal to the result belong to the rank largest.  The bits shared
-// by lo and hi are fixed up front; the rest are resolved 11 at a time, most
-// significant first, with an LDS histogram and a suffix scan per digit.
-template <int THREADS, typename ForEach>
-__device__ uint32_t radix_select(ForEach for_each, uint32_t lo, uint32_t hi, uint32_t rank, uint32_t& need,
-                                 TopkShared<THREADS / 64>& sh) {
+// Bin of sh.hist[0, kBins) that holds the need-th largest element (1 <= need
+// <= total), with the number of elements in higher bins (above) and in the
+// bin itself (count).  Ends with a barrier.
+template <int THREADS, int CAP>
+__device__ void pick_bin(uint32_t need, uint32_t& bin, uint32_t& above, uint32_t& count,
+                         TopkShared<THREADS / 64, CAP>& sh) {
   constexpr int NW = THREADS / 64;
   constexpr int DPT = kBins / THREADS;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  uint32_t mine[DPT];
+  uint32_t st = 0u;
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) {
+    mine[i] = sh.hist[tid * DPT + i];
+    st += mine[i];
+  }
+  uint32_t incl = st;   // suffix sum over this and higher lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = (uint32_t)__shfl_down((int)incl, o);
+    if (lane + o < 64) incl += v;
+  }
+  if (lane == 0) sh.w0[wave] = incl;
+  __syncthreads();
+  uint32_t ab = incl - st;
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+    if (w > wave) ab += sh.w0[w];
+  if (ab < need && need <= ab + st) {
+    uint32_t acc = ab;
+#pragma unroll
+    for (int i = DPT - 1; i >= 0; --i) {
+      if (acc < need && acc + mine[i] >= need) {
+        sh.digit = (uint32_t)(tid * DPT + i);
+        sh.above = acc;
+        sh.dcount = mine[i];
+      }
+      acc += mine[i];
+    }
+  }
+  __syncthreads();
+  bin = sh.digit;
+  above = sh.above;
+  count = sh.dcount;
+}
+
+// The rank-th largest code (1 <= rank <= count) of a multiset spread over the
+// workgroup, all inside [lo, hi]; for_each(visit) calls visit(code) on each of
+// the calling thread's codes.  Bits are resolved 11 at a time from the most
+// significant bit where lo and hi differ.  With slack = 0 the result is exact
+// and `need` returns how many elements equal to it belong to the rank
+// largest.  With slack > 0 the search may stop once the bin holding the rank
+// has at most slack elements and return that bin's lowest code: then between
+// rank and rank + slack - 1 elements are >= the result (`need` is not set).
+template <int THREADS, int CAP, typename ForEach>
+__device__ uint32_t radix_select(ForEach for_each, uint32_t lo, uint32_t hi, uint32_t rank, uint32_t slack,
+                                 uint32_t& need, TopkShared<THREADS / 64, CAP>& sh) {
+  constexpr int DPT = kBins / THREADS;
+  const int tid = threadIdx.x;
   need = rank;
   if (lo == hi) return hi;
   const int hb = 31 - __builtin_clz(lo ^ hi);
@@ -167,138 +240,149 @@ __device__ uint32_t radix_select(ForEach for_each, uint32_t lo, uint32_t hi, uin
       if ((v & pmask) == prefix) atomicAdd(&sh.hist[(v >> shift) & dmask], 1u);
     });
     __syncthreads();
-    uint32_t mine[DPT];
-    uint32_t st = 0u;
-#pragma unroll
-    for (int i = 0; i < DPT; ++i) {
-      mine[i] = sh.hist[tid * DPT + i];
-      st += mine[i];
-    }
-    uint32_t incl = st;   // suffix sum over this and higher lanes
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t v = (uint32_t)__shfl_down((int)incl, o);
-      if (lane + o < 64) incl += v;
-    }
-    if (lane == 0) sh.w0[wave] = incl;
-    __syncthreads();
-    uint32_t above = incl - st;
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-      if (w > wave) above += sh.w0[w];
-    if (above < need && need <= above + st) {
-      uint32_t acc = above;
-#pragma unroll
-      for (int i = DPT - 1; i >= 0; --i) {
-        if (acc < need && acc + mine[i] >= need) {
-          sh.digit = (uint32_t)(tid * DPT + i);
-          sh.above = acc;
-        }
-        acc += mine[i];
-      }
-    }
-    __syncthreads();
-    need -= sh.above;
-    prefix |= sh.digit << shift;
+    uint32_t digit, above, count;
+    pick_bin<THREADS, CAP>(need, digit, above, count, sh);
+    need -= above;
+    prefix |= digit << shift;
     pmask |= dmask << shift;
     top = shift - 1;
+    if (count <= slack) break;
   }
   return prefix;
 }
 
-// Block-wide reduction of (max, min, sum) over the workgroup.
 template <int NW>
-__device__ void block_max_min_sum(uint32_t& mx, uint32_t& mn, uint32_t& sm, TopkShared<NW>& sh) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  mx = wave_max_u32(mx);
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* w) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum_u32(v);
+  __syncthreads();
+  if (lane == 0) w[wave] = v;
+  __syncthreads();
+  uint32_t s = 0u;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) s += w[i];
+  return s;
+}
+
+// Workgroup min, max and sum in one exchange.
+template <int NW>
+__device__ __forceinline__ void block_min_max_sum(uint32_t& mn, uint32_t& mx, uint32_t& sm, uint32_t* w0,
+                                                  uint32_t* w1, uint32_t* w2) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
   sm = wave_sum_u32(sm);
-  __syncthreads();   // earlier readers of w0..w2 are done
+  __syncthreads();
   if (lane == 0) {
-    sh.w0[wave] = mx;
-    sh.w1[wave] = mn;
-    sh.w2[wave] = sm;
+    w0[wave] = mn;
+    w1[wave] = mx;
+    w2[wave] = sm;
   }
   __syncthreads();
-  mx = 0u;
   mn = 0xffffffffu;
+  mx = 0u;
   sm = 0u;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    mx = max(mx, sh.w0[w]);
-    mn = min(mn, sh.w1[w]);
-    sm += sh.w2[w];
+  for (int i = 0; i < NW; ++i) {
+    mn = min(mn, w0[i]);
+    mx = max(mx, w1[i]);
+    sm += w2[i];
   }
 }
 
-// Exclusive prefix sums over threads (thread order) of two per-thread counts.
-template <int NW>
-__device__ void block_excl_scan2(uint32_t a, uint32_t b, uint32_t& a_before, uint32_t& b_before,
-                                 TopkShared<NW>& sh) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  uint32_t ia = a, ib = b;
+// Exclusive prefix popcounts of bitmap words [0, nwords) into pre[].
+template <int THREADS>
+__device__ __forceinline__ void bitmap_prefix(const uint32_t* bits, uint32_t* pre, int nwords, uint32_t* w) {
+  constexpr int NW = THREADS / 64;
+  constexpr int WPT = (kBitmapWords + THREADS - 1) / THREADS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t local[WPT];
+  uint32_t sum = 0u;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int wi = tid * WPT + i;
+    local[i] = wi < nwords ? (uint32_t)__popc(bits[wi]) : 0u;
+    sum += local[i];
+  }
+  uint32_t incl = sum;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t ta = (uint32_t)__shfl_up((int)ia, o);
-    const uint32_t tb = (uint32_t)__shfl_up((int)ib, o);
-    if (lane >= o) {
-      ia += ta;
-      ib += tb;
-    }
+    const uint32_t v = (uint32_t)__shfl_up((int)incl, o);
+    if (lane >= o) incl += v;
   }
   __syncthreads();
-  if (lane == 63) {
-    sh.w0[wave] = ia;
-    sh.w1[wave] = ib;
-  }
+  if (lane == 63) w[wave] = incl;
   __syncthreads();
-  a_before = ia - a;
-  b_before = ib - b;
+  uint32_t run = incl - sum;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    if (w < wave) {
-      a_before += sh.w0[w];
-      b_before += sh.w1[w];
-    }
+  for (int i = 0; i < NW; ++i)
+    if (i < wave) run += w[i];
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int wi = tid * WPT + i;
+    if (wi < nwords) pre[wi] = run;
+    run += local[i];
   }
+  __syncthreads();
 }
 
-template <bool LEVEL0, bool FINAL>
-struct Emitter {
-  const TopkKernelArgs& a;
-  int64_t sa;
-  int64_t row;
-  int64_t out_base;
-  int req;
-  int row_ks;
-  __device__ __forceinline__ void operator()(uint32_t o, uint32_t pos, uint32_t key) const {
-    int32_t j;
-    if (LEVEL0) j = (int32_t)(sa + pos);
-    else j = a.in_idx[row * a.in_len + sa + pos];
-    if (FINAL) {
-      a.out[out_base + o] = map_index(a.map, req, row_ks, j);
+__device__ __forceinline__ uint32_t bitmap_rank(const uint32_t* bits, const uint32_t* pre, uint32_t pos) {
+  const uint32_t w = pos >> 5;
+  return pre[w] + (uint32_t)__popc(bits[w] & ((1u << (pos & 31)) - 1u));
+}
+
+// The keys of one segment as codes, addressed by position from a load base
+// rounded down to VEC elements; valid positions are [off, span).
+template <bool LEVEL0, int VEC>
+struct SegmentSource {
+  const float* f;       // level 0: logits at the load base
+  const uint32_t* u;    // other levels: codes at the load base
+  int off;
+  int span;
+
+  __device__ __forceinline__ static uint32_t float_code(float x) { return max(float_to_ordered(x), 1u); }
+
+  // codes of positions [v * VEC, v * VEC + VEC)
+  __device__ __forceinline__ void load(int v, uint32_t* c) const {
+    if (LEVEL0) {
+      if (VEC == 4) {
+        const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(f) + v);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) c[i] = float_code(t[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) c[i] = float_code(__builtin_nontemporal_load(f + v * VEC + i));
+      }
     } else {
-      a.out_keys[out_base + o] = key;
-      a.out_idx[out_base + o] = j;
+      if (VEC == 4) {
+        const v4i t = *(reinterpret_cast<const v4i*>(u) + v);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) c[i] = (uint32_t)t[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) c[i] = u[v * VEC + i];
+      }
     }
   }
+  __device__ __forceinline__ uint32_t code_at(int pos) const { return LEVEL0 ? float_code(f[pos]) : u[pos]; }
+  __device__ __forceinline__ bool valid(int pos) const { return pos >= off && pos < span; }
 };
 
-template <int THREADS, int VPT, bool LEVEL0, bool FINAL>
+template <int THREADS, int CAP, bool LEVEL0, bool FINAL, int VEC>
 __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
   constexpr int NW = THREADS / 64;
+  constexpr int UNR = kElemsPerPass / VEC;   // vectors per thread per pass
   static_assert(kBins % THREADS == 0, "bins per thread");
-  __shared__ TopkShared<NW> sh;
+  static_assert(CAP >= kBitmapWords, "fallback bitmaps reuse the candidate list");
+  static_assert(THREADS == kTopkThreads, "sample runs are one workgroup wide");
+  __shared__ TopkShared<NW, CAP> sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
   const int row = blockIdx.x / a.nseg;
   const int seg = blockIdx.x - row * a.nseg;
 
-  // ---- segment window -------------------------------------------------------
+  // ---- segment window --------------------------------------------------------
   int row_ks = 0;
   int64_t sa = 0;
   int len = 0;
@@ -314,189 +398,295 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
     sa = (int64_t)seg * a.seg_len;
     len = (int)max((int64_t)0, min((int64_t)a.seg_len, a.in_len - sa));
   }
-
-  // ---- load keys into VGPRs -------------------------------------------------
-  // Loads are unconditional from a clamped in-bounds position (len >= 1);
-  // positions past the segment are then replaced by the padding key 0.
-  uint32_t key[VPT];
-  const int base = wave * (64 * VPT) + lane;
-  const int last = max(len - 1, 0);
-  if (len == 0) {
-#pragma unroll
-    for (int p = 0; p < VPT; ++p) key[p] = 0u;
-  } else if (LEVEL0) {
-    const float* src = a.logits + (int64_t)row * a.ld + sa;
-    // all VPT loads are issued before any is consumed: the padding mask is
-    // applied arithmetically so no load sits under a branch
-#pragma unroll
-    for (int p = 0; p < VPT; ++p) key[p] = __float_as_uint(__builtin_nontemporal_load(src + min(base + p * 64, last)));
-#pragma unroll
-    for (int p = 0; p < VPT; ++p) {
-      const uint32_t keep = 0u - (uint32_t)(base + p * 64 < len);
-      key[p] = max(float_to_ordered(__uint_as_float(key[p])), 1u) & keep;
-    }
-  } else {
-    const uint32_t* src = a.in_keys + (int64_t)row * a.in_len + sa;
-#pragma unroll
-    for (int p = 0; p < VPT; ++p) key[p] = src[min(base + p * 64, last)];
-#pragma unroll
-    for (int p = 0; p < VPT; ++p) key[p] &= 0u - (uint32_t)(base + p * 64 < len);
-  }
-
-  // ---- valid count, min and max ---------------------------------------------
-  uint32_t kmax = 0u, kmin = 0xffffffffu, cnt = 0u;
-#pragma unroll
-  for (int p = 0; p < VPT; ++p) {
-    const uint32_t v = key[p];
-    if (v != 0u) {
-      kmax = max(kmax, v);
-      kmin = min(kmin, v);
-      ++cnt;
-    }
-  }
-  block_max_min_sum<NW>(kmax, kmin, cnt, sh);
-  const uint32_t kk = min((uint32_t)a.k, cnt);
+  const int64_t lb = sa & ~(int64_t)(VEC - 1);
+  SegmentSource<LEVEL0, VEC> src;
+  src.f = LEVEL0 ? a.logits + (int64_t)row * a.ld + lb : nullptr;
+  src.u = LEVEL0 ? nullptr : a.in_keys + (int64_t)row * a.in_len + lb;
+  src.off = (int)(sa - lb);
+  src.span = src.off + len;
+  const int nvec = (src.span + VEC - 1) / VEC;
 
   const int64_t out_base = FINAL ? (int64_t)row * a.ld_out : ((int64_t)row * a.nseg + seg) * (int64_t)a.k;
-  Emitter<LEVEL0, FINAL> emit{a, sa, row, out_base, FINAL ? map_request(a.map, a.row0 + row) : 0, row_ks};
-
-  if (kk > 0u) {
-    // ---- candidate threshold T from a strided sample ---------------------------
-    // Target: about 1.25 * kk + 16 sample-strides of elements at or above T, so
-    // that the exact k-th key is almost always among the candidates.
-    uint32_t T = 1u;   // 1 = every valid key
-    if (cnt > (uint32_t)kCandCap) {
-      uint32_t smax = 0u, smin = 0xffffffffu, ns = 0u;
-#pragma unroll
-      for (int p = 0; p < VPT; p += kSampleStride) {
-        const uint32_t v = key[p];
-        if (v != 0u) {
-          smax = max(smax, v);
-          smin = min(smin, v);
-          ++ns;
-        }
-      }
-      block_max_min_sum<NW>(smax, smin, ns, sh);
-      const uint64_t want = ((uint64_t)kk * ns * 5u + 4ull * cnt - 1u) / (4ull * cnt) + 16u;
-      if (ns > 0u && want < ns) {
-        uint32_t unused;
-        T = radix_select<THREADS>(
-            [&](auto&& visit) {
-#pragma unroll
-              for (int p = 0; p < VPT; p += kSampleStride)
-                if (key[p] != 0u) visit(key[p]);
-            },
-            smin, smax, (uint32_t)want, unused, sh);
-      }
-    }
-
-    // ---- count candidates (keys >= T) per wave --------------------------------
-    uint32_t cw = 0u;
-#pragma unroll
-    for (int p = 0; p < VPT; ++p) cw += (uint32_t)__popcll(ballot64(key[p] >= T));
-    __syncthreads();
-    if (lane == 0) sh.w2[wave] = cw;
-    __syncthreads();
-    uint32_t C = 0u, woff = 0u;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const uint32_t x = sh.w2[w];
-      if (w < wave) woff += x;
-      C += x;
-    }
-
-    if (C >= kk && C <= (uint32_t)kCandCap) {
-      // ---- ordered compaction of the candidates into LDS -----------------------
-      uint32_t off = woff;
-#pragma unroll
-      for (int p = 0; p < VPT; ++p) {
-        const bool c = key[p] >= T;
-        const uint64_t b = ballot64(c);
-        if (c) {
-          const uint32_t o = off + mbcnt64(b);
-          sh.ck[o] = key[p];
-          sh.cp[o] = (uint32_t)(base + p * 64);
-        }
-        off += (uint32_t)__popcll(b);
-      }
-      __syncthreads();
-      // ---- exact threshold among the candidates --------------------------------
-      uint32_t need;
-      const uint32_t tau = radix_select<THREADS>(
-          [&](auto&& visit) {
-            for (uint32_t i = tid; i < C; i += THREADS) visit(sh.ck[i]);
-          },
-          T, kmax, kk, need, sh);
-      // ---- emission in position order ------------------------------------------
-      const uint32_t per = (C + THREADS - 1) / THREADS;
-      const uint32_t c0 = min(C, (uint32_t)tid * per);
-      const uint32_t c1 = min(C, c0 + per);
-      uint32_t gt = 0u, eq = 0u;
-      for (uint32_t i = c0; i < c1; ++i) {
-        const uint32_t v = sh.ck[i];
-        gt += v > tau;
-        eq += v == tau;
-      }
-      uint32_t gt_before, eq_before;
-      block_excl_scan2<NW>(gt, eq, gt_before, eq_before, sh);
-      uint32_t run_eq = eq_before;
-      uint32_t run_sel = gt_before + min(eq_before, need);
-      for (uint32_t i = c0; i < c1; ++i) {
-        const uint32_t v = sh.ck[i];
-        bool sel = v > tau;
-        if (v == tau) {
-          sel = run_eq < need;
-          ++run_eq;
-        }
-        if (sel) {
-          emit(run_sel, sh.cp[i], v);
-          ++run_sel;
-        }
-      }
+  const int req = FINAL ? map_request(a.map, a.row0 + row) : 0;
+  auto emit = [&](uint32_t slot, uint32_t pos, uint32_t code) {
+    int32_t j;
+    if (LEVEL0) j = (int32_t)(lb + pos);
+    else j = a.in_idx[(int64_t)row * a.in_len + lb + pos];
+    if (FINAL) {
+      a.out[out_base + slot] = map_index(a.map, req, row_ks, j);
     } else {
-      // ---- fallback: exact select over every key in registers -------------------
-      uint32_t need;
-      const uint32_t tau = radix_select<THREADS>(
-          [&](auto&& visit) {
+      a.out_keys[out_base + slot] = code;
+      a.out_idx[out_base + slot] = j;
+    }
+  };
+  // One pass over the segment: visit(pos, code) for every valid non-padding key.
+  auto stream = [&](auto&& visit) {
+    for (int vb = 0; vb < nvec; vb += THREADS * UNR) {
+      const int v0 = vb + tid;
+      uint32_t c[UNR][VEC];
 #pragma unroll
-            for (int p = 0; p < VPT; ++p)
-              if (key[p] != 0u) visit(key[p]);
-          },
-          kmin, kmax, kk, need, sh);
-      uint32_t gt = 0u, eq = 0u;
-#pragma unroll
-      for (int p = 0; p < VPT; ++p) {
-        gt += (uint32_t)__popcll(ballot64(key[p] > tau));
-        eq += (uint32_t)__popcll(ballot64(key[p] == tau));
+      for (int u = 0; u < UNR; ++u) {
+        const int v = min(v0 + u * THREADS, nvec - 1);
+        src.load(v, c[u]);
       }
-      __syncthreads();
-      if (lane == 0) {
-        sh.w0[wave] = gt;
-        sh.w1[wave] = eq;
-      }
-      __syncthreads();
-      uint32_t gt_before = 0u, eq_before = 0u;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        if (w < wave) {
-          gt_before += sh.w0[w];
-          eq_before += sh.w1[w];
+      for (int u = 0; u < UNR; ++u) {
+        const int v = v0 + u * THREADS;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const int pos = v * VEC + i;
+          if (v < nvec && src.valid(pos) && c[u][i] != 0u) visit(pos, c[u][i]);
         }
       }
-      uint32_t run_eq = eq_before;
-      uint32_t run_sel = gt_before + min(eq_before, need);
+    }
+  };
+
+  // ---- LDS state of the candidate list ---------------------------------------
+  const int nwords = (src.span + 31) / 32;
+  for (int wi = tid; wi < nwords; wi += THREADS) sh.bits[wi] = 0u;
+  if (tid == 0) {
+    sh.cnt = 0u;
+    sh.nb = 0u;
+  }
+
+  // ---- 1. candidate threshold ------------------------------------------------
+  uint32_t T = 1u;          // lowest candidate code; 1 takes every key
+  bool sampled = false;     // T came from the sample
+  bool try_list = true;     // false: the list cannot hold the candidates
+  uint32_t bshift = 0u;     // candidate bins: min((code - T) >> bshift, kBins - 1)
+  uint32_t kk = (uint32_t)min(a.k, len);   // level 0: every position of the window is a key
+  if (len > CAP) {
+    uint32_t sc[kSampleRuns];
 #pragma unroll
-      for (int p = 0; p < VPT; ++p) {
-        const uint32_t v = key[p];
-        const bool is_gt = v > tau;
-        const bool is_eq = v == tau;
-        const uint64_t beq = ballot64(is_eq);
-        const bool sel = is_gt || (is_eq && (run_eq + mbcnt64(beq)) < need);
-        const uint64_t bsel = ballot64(sel);
-        if (sel) emit(run_sel + mbcnt64(bsel), (uint32_t)(base + p * 64), v);
-        run_eq += (uint32_t)__popcll(beq);
-        run_sel += (uint32_t)__popcll(bsel);
+    for (int b = 0; b < kSampleRuns; ++b) {
+      const int start = src.off + (int)((int64_t)b * (len - THREADS) / (kSampleRuns - 1));
+      sc[b] = src.code_at(start + tid);
+    }
+    uint32_t smin = 0xffffffffu, smax = 0u, ns = 0u;
+#pragma unroll
+    for (int b = 0; b < kSampleRuns; ++b) {
+      if (sc[b] != 0u) {
+        smin = min(smin, sc[b]);
+        smax = max(smax, sc[b]);
+        ++ns;
       }
+    }
+    block_min_max_sum<NW>(smin, smax, ns, sh.w0, sh.w1, sh.w2);
+    // sample rank whose code should leave ~1.3 k keys at or above it
+    const uint64_t want = ((uint64_t)kk * kSampleSize * 13u + 10ull * len - 1u) / (10ull * len) + 16u;
+    if (ns > 0u && want < ns && want * (uint64_t)len <= (uint64_t)CAP * kSampleSize * 7u / 8u) {
+      uint32_t unused;
+      T = radix_select<THREADS, CAP>(
+          [&](auto&& visit) {
+#pragma unroll
+            for (int b = 0; b < kSampleRuns; ++b)
+              if (sc[b] != 0u) visit(sc[b]);
+          },
+          smin, smax, (uint32_t)want, 16u, unused, sh);
+      T = max(T, 1u);
+      sampled = true;
+      const uint32_t range = smax - min(T, smax);
+      bshift = range >> kDigitBits ? (uint32_t)(32 - __builtin_clz(range) - kDigitBits) : 0u;
+    } else if (LEVEL0) {
+      try_list = false;   // every key would be a candidate, more than the list holds
+    }
+  }
+  if (sampled) {
+#pragma unroll
+    for (int i = 0; i < kBins / THREADS; ++i) sh.hist[tid * (kBins / THREADS) + i] = 0u;
+  }
+  __syncthreads();
+  auto cand_bin = [&](uint32_t code) { return min((code - T) >> bshift, (uint32_t)(kBins - 1)); };
+
+  // ---- 2. compaction of the codes >= T ----------------------------------------
+  uint32_t C = 0xffffffffu;
+  if (try_list) {
+    // Every lane runs every pass (the slot scan below is wave-wide); the next
+    // pass's loads are in flight while this pass's keys are appended.
+    constexpr int kPass = THREADS * UNR;
+    auto load_pass = [&](int vb, uint32_t (&dst)[UNR][VEC]) {
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) src.load(min(vb + tid + u * THREADS, nvec - 1), dst[u]);
+    };
+    uint32_t c[UNR][VEC];
+    if (nvec > 0) load_pass(0, c);
+    for (int vb = 0; vb < nvec; vb += kPass) {
+      uint32_t nx[UNR][VEC];
+      const bool more = vb + kPass < nvec;
+      if (more) load_pass(vb + kPass, nx);
+      const int v0 = vb + tid;
+      uint32_t mask = 0u;
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int v = v0 + u * THREADS;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const int pos = v * VEC + i;
+          const bool cand = v < nvec && src.valid(pos) && c[u][i] >= T;
+          mask |= (uint32_t)cand << (u * VEC + i);
+        }
+      }
+      // claim slots for the wave's candidates: exclusive scan of the counts
+      const uint32_t mine = (uint32_t)__popc(mask);
+      uint32_t incl = mine;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = (uint32_t)__shfl_up((int)incl, o);
+        if (lane >= o) incl += t;
+      }
+      const uint32_t total = (uint32_t)__shfl((int)incl, 63);
+      if (total != 0u) {
+        uint32_t base = 0u;
+        if (lane == 63) base = atomicAdd(&sh.cnt, total);
+        uint32_t slot = (uint32_t)__shfl((int)base, 63) + incl - mine;
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) {
+            if (mask & (1u << (u * VEC + i))) {
+              if (slot < (uint32_t)CAP) sh.cand[slot] = v2u{c[u][i], (uint32_t)((v0 + u * THREADS) * VEC + i)};
+              ++slot;
+            }
+          }
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) c[u][i] = nx[u][i];
+      }
+    }
+    __syncthreads();
+    C = sh.cnt;
+    if (!LEVEL0 && !sampled) kk = min((uint32_t)a.k, C);   // C counted every key
+  }
+
+  bool done = false;
+  if (kk > 0u && C >= kk && C <= (uint32_t)CAP) {
+    if (sampled) {
+      // ---- 3. the bin of the k-th candidate ------------------------------------
+      for (uint32_t i = tid; i < C; i += THREADS) atomicAdd(&sh.hist[cand_bin(sh.cand[i].x)], 1u);
+      __syncthreads();
+      uint32_t b, above, m;
+      pick_bin<THREADS, CAP>(kk, b, above, m, sh);
+      if (m <= (uint32_t)kBoundaryMax) {
+        const uint32_t need = kk - above;   // taken from the boundary bin, 1 <= need <= m
+        for (uint32_t i = tid; i < C; i += THREADS) {
+          const v2u e = sh.cand[i];
+          const uint32_t code = e.x, pos = e.y;
+          const uint32_t bn = cand_bin(code);
+          if (bn > b) {
+            atomicOr(&sh.bits[pos >> 5], 1u << (pos & 31));
+          } else if (bn == b) {
+            const uint32_t o = atomicAdd(&sh.nb, 1u);
+            sh.bk[o] = code;
+            sh.bp[o] = pos;
+          }
+        }
+        __syncthreads();
+        // ---- 4. rank the boundary bin pairwise: value desc, then position asc ----
+        if (tid < (int)m) {
+          const uint32_t mc = sh.bk[tid], mp = sh.bp[tid];
+          uint32_t r = 0u;
+          for (uint32_t j = 0; j < m; ++j) {
+            const uint32_t c2 = sh.bk[j], p2 = sh.bp[j];
+            r += (c2 > mc) || (c2 == mc && p2 < mp);
+          }
+          if (r < need) atomicOr(&sh.bits[mp >> 5], 1u << (mp & 31));
+        }
+        __syncthreads();
+        // ---- 5. output slots by position --------------------------------------
+        bitmap_prefix<THREADS>(sh.bits, sh.hist, nwords, sh.w0);
+        for (uint32_t i = tid; i < C; i += THREADS) {
+          const v2u e = sh.cand[i];
+          if ((sh.bits[e.y >> 5] >> (e.y & 31)) & 1u) emit(bitmap_rank(sh.bits, sh.hist, e.y), e.y, e.x);
+        }
+        done = true;
+      }
+    }
+    if (!done) {
+      // ---- exact selection on the whole list (dense ties, or an unsampled list) ----
+      uint32_t cmin = 0xffffffffu, cmax = 0u, unused = 0u;
+      for (uint32_t i = tid; i < C; i += THREADS) {
+        cmin = min(cmin, sh.cand[i].x);
+        cmax = max(cmax, sh.cand[i].x);
+      }
+      block_min_max_sum<NW>(cmin, cmax, unused, sh.w0, sh.w1, sh.w2);
+      uint32_t need;
+      const uint32_t tau = radix_select<THREADS, CAP>(
+          [&](auto&& visit) {
+            for (uint32_t i = tid; i < C; i += THREADS) visit(sh.cand[i].x);
+          },
+          cmin, cmax, kk, 0u, need, sh);
+      uint32_t eq = 0u;
+      for (uint32_t i = tid; i < C; i += THREADS) eq += sh.cand[i].x == tau;
+      const uint32_t E = block_sum<NW>(eq, sh.w0);
+      if (need < E) {
+        for (int wi = tid; wi < nwords; wi += THREADS) sh.bits[wi] = 0u;
+        __syncthreads();
+        for (uint32_t i = tid; i < C; i += THREADS)
+          if (sh.cand[i].x == tau) atomicOr(&sh.bits[sh.cand[i].y >> 5], 1u << (sh.cand[i].y & 31));
+        __syncthreads();
+        bitmap_prefix<THREADS>(sh.bits, sh.hist, nwords, sh.w0);
+        // ties past the first `need` by position drop out: code 0 is below tau
+        for (uint32_t i = tid; i < C; i += THREADS)
+          if (sh.cand[i].x == tau && bitmap_rank(sh.bits, sh.hist, sh.cand[i].y) >= need) sh.cand[i].x = 0u;
+        __syncthreads();
+      }
+      for (int wi = tid; wi < nwords; wi += THREADS) sh.bits[wi] = 0u;
+      __syncthreads();
+      for (uint32_t i = tid; i < C; i += THREADS)
+        if (sh.cand[i].x >= tau) atomicOr(&sh.bits[sh.cand[i].y >> 5], 1u << (sh.cand[i].y & 31));
+      __syncthreads();
+      bitmap_prefix<THREADS>(sh.bits, sh.hist, nwords, sh.w0);
+      for (uint32_t i = tid; i < C; i += THREADS) {
+        const v2u e = sh.cand[i];
+        if (e.x >= tau) emit(bitmap_rank(sh.bits, sh.hist, e.y), e.y, e.x);
+      }
+      done = true;
+    }
+  }
+  if (!done && len > 0) {
+    // ---- fallback: exact selection over every key of the segment, streamed --------
+    if (!LEVEL0) {
+      uint32_t nv = 0u;
+      stream([&](int, uint32_t) { ++nv; });
+      kk = min((uint32_t)a.k, block_sum<NW>(nv, sh.w0));
+    }
+    if (kk > 0u) {
+      uint32_t need;
+      const uint32_t tau = radix_select<THREADS, CAP>(
+          [&](auto&& visit) { stream([&](int, uint32_t code) { visit(code); }); }, 1u, 0xffffffffu, kk, 0u,
+          need, sh);
+      uint32_t* tie_bits = reinterpret_cast<uint32_t*>(sh.cand);   // the candidate list is free here
+      uint32_t* tie_pre = tie_bits + kBitmapWords;
+      uint32_t eq = 0u;
+      stream([&](int, uint32_t code) { eq += code == tau; });
+      const uint32_t E = block_sum<NW>(eq, sh.w0);
+      const bool rank_ties = need < E;
+      if (rank_ties) {
+        for (int wi = tid; wi < nwords; wi += THREADS) tie_bits[wi] = 0u;
+        __syncthreads();
+        stream([&](int pos, uint32_t code) {
+          if (code == tau) atomicOr(&tie_bits[pos >> 5], 1u << (pos & 31));
+        });
+        __syncthreads();
+        bitmap_prefix<THREADS>(tie_bits, tie_pre, nwords, sh.w0);
+      }
+      auto selected = [&](int pos, uint32_t code) {
+        return code > tau || (code == tau && (!rank_ties || bitmap_rank(tie_bits, tie_pre, pos) < need));
+      };
+      for (int wi = tid; wi < nwords; wi += THREADS) sh.bits[wi] = 0u;
+      __syncthreads();
+      stream([&](int pos, uint32_t code) {
+        if (selected(pos, code)) atomicOr(&sh.bits[pos >> 5], 1u << (pos & 31));
+      });
+      __syncthreads();
+      bitmap_prefix<THREADS>(sh.bits, sh.hist, nwords, sh.w0);
+      stream([&](int pos, uint32_t code) {
+        if (selected(pos, code)) emit(bitmap_rank(sh.bits, sh.hist, (uint32_t)pos), (uint32_t)pos, code);
+      });
     }
   }
   // padding after the kk selected entries
@@ -512,27 +702,13 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
 
 // ---- host-side plan and launch ----------------------------------------------
 
-struct TopkCfg {
-  int threads;
-  int vpt;
-  int cap;
-};
-constexpr TopkCfg kTopkCfgs[] = {{256, 16, 4096}, {512, 32, 16384}, {512, 64, 32768}, {512, 128, 65536}};
-constexpr int kNumTopkCfgs = 4;
-constexpr int64_t kMaxSeg = 65536;
-
-static int pick_cfg(int64_t seg_len) {
-  for (int c = 0; c < kNumTopkCfgs; ++c)
-    if (seg_len <= kTopkCfgs[c].cap) return c;
-  return kNumTopkCfgs - 1;
-}
-
 TopkPlan plan_topk(int32_t rows, int64_t width, int32_t k) {
   TopkPlan p{};
   p.buf_bytes[0] = p.buf_bytes[1] = 0;
   int64_t in_len = width > 0 ? width : 1;
+  // few rows: split long windows so about this many workgroups run
   const int64_t target_wgs = 1024;
-  const int64_t min_seg = std::max<int64_t>(4 * (int64_t)k, 4096);
+  const int64_t min_seg = std::max<int64_t>(8 * (int64_t)k, 16384);
   for (int lvl = 0; lvl < kMaxTopkLevels; ++lvl) {
     int64_t nseg = (in_len + kMaxSeg - 1) / kMaxSeg;
     if (lvl == 0 && in_len > min_seg && rows > 0 && rows < target_wgs) {
@@ -546,7 +722,7 @@ TopkPlan plan_topk(int32_t rows, int64_t width, int32_t k) {
     L.in_len = in_len;
     L.seg_len = (int32_t)seg_len;
     L.nseg = (int32_t)nseg;
-    L.cfg = pick_cfg(seg_len);
+    L.cfg = topk_needs_big_cap(k) ? 1 : 0;
     p.nlevels = lvl + 1;
     if (nseg == 1) break;
     const int64_t out_len = nseg * (int64_t)k;
@@ -566,16 +742,21 @@ size_t topk_workspace_bytes(const TopkPlan& p) {
   return total;
 }
 
-template <int THREADS, int VPT>
-static void launch_cfg(bool level0, bool final_level, unsigned grid, const TopkKernelArgs& a, hipStream_t s) {
-  if (level0 && final_level)
-    hipLaunchKernelGGL((topk_kernel<THREADS, VPT, true, true>), dim3(grid), dim3(THREADS), 0, s, a);
-  else if (level0)
-    hipLaunchKernelGGL((topk_kernel<THREADS, VPT, true, false>), dim3(grid), dim3(THREADS), 0, s, a);
-  else if (final_level)
-    hipLaunchKernelGGL((topk_kernel<THREADS, VPT, false, true>), dim3(grid), dim3(THREADS), 0, s, a);
+template <int CAP, bool LEVEL0, bool FINAL>
+static void launch_vec(bool vec4, unsigned grid, const TopkKernelArgs& a, hipStream_t s) {
+  if (vec4)
+    hipLaunchKernelGGL((topk_kernel<kTopkThreads, CAP, LEVEL0, FINAL, 4>), dim3(grid), dim3(kTopkThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((topk_kernel<THREADS, VPT, false, false>), dim3(grid), dim3(THREADS), 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<kTopkThreads, CAP, LEVEL0, FINAL, 1>), dim3(grid), dim3(kTopkThreads), 0, s, a);
+}
+
+template <int CAP>
+static void launch_cap(bool level0, bool final_level, bool vec4, unsigned grid, const TopkKernelArgs& a,
+                       hipStream_t s) {
+  if (level0 && final_level) launch_vec<CAP, true, true>(vec4, grid, a, s);
+  else if (level0) launch_vec<CAP, true, false>(vec4, grid, a, s);
+  else if (final_level) launch_vec<CAP, false, true>(vec4, grid, a, s);
+  else launch_vec<CAP, false, false>(vec4, grid, a, s);
 }
 
 hipError_t launch_topk(const TopkArgs& ta, const TopkPlan& plan, void* ws, hipStream_t s) {
@@ -606,12 +787,17 @@ hipError_t launch_topk(const TopkArgs& ta, const TopkPlan& plan, void* ws, hipSt
     a.k = ta.k;
     a.row0 = ta.row0;
     a.map = ta.map;
+    bool vec4;
     if (!level0) {
       const uint8_t* src = bufs[(lvl - 1) & 1];
       const int64_t n_in = (int64_t)ta.rows * L.in_len;
       a.in_keys = reinterpret_cast<const uint32_t*>(src);
       a.in_idx = reinterpret_cast<const int32_t*>(src + (size_t)n_in * 4u);
       a.in_len = L.in_len;
+      vec4 = (L.in_len % 4) == 0;
+    } else {
+      // 16-byte loads need every row start 16-byte aligned
+      vec4 = (ta.ld % 4) == 0 && (reinterpret_cast<uintptr_t>(ta.logits) & 15u) == 0;
     }
     if (final_level) {
       a.out = ta.out;
@@ -624,12 +810,8 @@ hipError_t launch_topk(const TopkArgs& ta, const TopkPlan& plan, void* ws, hipSt
     }
     const int64_t grid = (int64_t)ta.rows * L.nseg;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    switch (L.cfg) {
-      case 0: launch_cfg<256, 16>(level0, final_level, (unsigned)grid, a, s); break;
-      case 1: launch_cfg<512, 32>(level0, final_level, (unsigned)grid, a, s); break;
-      case 2: launch_cfg<512, 64>(level0, final_level, (unsigned)grid, a, s); break;
-      default: launch_cfg<512, 128>(level0, final_level, (unsigned)grid, a, s); break;
-    }
+    if (L.cfg == 1) launch_cap<kBigCap>(level0, final_level, vec4, (unsigned)grid, a, s);
+    else launch_cap<kSmallCap>(level0, final_level, vec4, (unsigned)grid, a, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
