@@ -109,7 +109,7 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   return v;
 }
 
-__device__ __forceinline__ int32_t map_index(const TopkMap& m, int req, int row_ks, int32_t j) {
+__device__ __forceinline__ int32_t map_index(const TopkMap m, int req, int row_ks, int32_t j) {
   if (m.kind == FP8IDX_MAP_TOKEN_TABLE) {
     const int64_t pos = (int64_t)j - row_ks;
     if (req < 0 || pos < 0 || pos >= m.ld) return -1;
@@ -126,7 +126,7 @@ __device__ __forceinline__ int32_t map_index(const TopkMap& m, int req, int row_
 }
 
 // Request of a global row under the map (uniform per workgroup).
-__device__ __forceinline__ int map_request(const TopkMap& m, int grow) {
+__device__ __forceinline__ int map_request(const TopkMap m, int grow) {
   if (m.kind == FP8IDX_MAP_TOKEN_TABLE) {
     if (m.cu_rows == nullptr) return 0;
     // largest r in [0, num_req) with cu_rows[r] <= grow
@@ -407,13 +407,14 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
   const int nvec = (src.span + VEC - 1) / VEC;
 
   const int64_t out_base = FINAL ? (int64_t)row * a.ld_out : ((int64_t)row * a.nseg + seg) * (int64_t)a.k;
-  const int req = FINAL ? map_request(a.map, a.row0 + row) : 0;
+  const TopkMap map = a.map;
+  const int req = FINAL ? map_request(map, a.row0 + row) : 0;
   auto emit = [&](uint32_t slot, uint32_t pos, uint32_t code) {
     int32_t j;
     if (LEVEL0) j = (int32_t)(lb + pos);
     else j = a.in_idx[(int64_t)row * a.in_len + lb + pos];
     if (FINAL) {
-      a.out[out_base + slot] = map_index(a.map, req, row_ks, j);
+      a.out[out_base + slot] = map_index(map, req, row_ks, j);
     } else {
       a.out_keys[out_base + slot] = code;
       a.out_idx[out_base + slot] = j;
@@ -563,25 +564,49 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
   }
 
   bool done = false;
+  bool row_written = false;   // output row including padding already stored
   if (kk > 0u && C >= kk && C <= (uint32_t)CAP) {
     if (sampled) {
       // ---- 3. the bin of the k-th candidate ------------------------------------
-      for (uint32_t i = tid; i < C; i += THREADS) atomicAdd(&sh.hist[cand_bin(sh.cand[i].x)], 1u);
+      // Each thread handles list entries tid + THREADS * j in chunks of kRegPairs
+      // held in registers (one chunk, read once, when the list is small).
+      constexpr int kLpt = CAP / THREADS;
+      constexpr int kRegPairs = kLpt < 16 ? kLpt : 16;
+      constexpr int kChunks = kLpt / kRegPairs;
+      v2u reg[kRegPairs];
+      auto load_chunk = [&](int ch) {
+#pragma unroll
+        for (int j = 0; j < kRegPairs; ++j) {
+          const uint32_t i = (uint32_t)((ch * kRegPairs + j) * THREADS + tid);
+          reg[j] = i < C ? sh.cand[i] : v2u{0u, 0u};   // code 0: no entry (all candidates are >= T >= 1)
+        }
+      };
+      if (kChunks == 1) load_chunk(0);
+      for (int ch = 0; ch < kChunks; ++ch) {
+        if (kChunks > 1) load_chunk(ch);
+#pragma unroll
+        for (int j = 0; j < kRegPairs; ++j)
+          if (reg[j].x != 0u) atomicAdd(&sh.hist[cand_bin(reg[j].x)], 1u);
+      }
       __syncthreads();
       uint32_t b, above, m;
       pick_bin<THREADS, CAP>(kk, b, above, m, sh);
       if (m <= (uint32_t)kBoundaryMax) {
         const uint32_t need = kk - above;   // taken from the boundary bin, 1 <= need <= m
-        for (uint32_t i = tid; i < C; i += THREADS) {
-          const v2u e = sh.cand[i];
-          const uint32_t code = e.x, pos = e.y;
-          const uint32_t bn = cand_bin(code);
-          if (bn > b) {
-            atomicOr(&sh.bits[pos >> 5], 1u << (pos & 31));
-          } else if (bn == b) {
-            const uint32_t o = atomicAdd(&sh.nb, 1u);
-            sh.bk[o] = code;
-            sh.bp[o] = pos;
+        for (int ch = 0; ch < kChunks; ++ch) {
+          if (kChunks > 1) load_chunk(ch);
+#pragma unroll
+          for (int j = 0; j < kRegPairs; ++j) {
+            if (reg[j].x == 0u) continue;
+            const uint32_t bn = cand_bin(reg[j].x);
+            const uint32_t pos = reg[j].y;
+            if (bn > b) {
+              atomicOr(&sh.bits[pos >> 5], 1u << (pos & 31));
+            } else if (bn == b) {
+              const uint32_t o = atomicAdd(&sh.nb, 1u);
+              sh.bk[o] = reg[j].x;
+              sh.bp[o] = pos;
+            }
           }
         }
         __syncthreads();
@@ -598,9 +623,39 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
         __syncthreads();
         // ---- 5. output slots by position --------------------------------------
         bitmap_prefix<THREADS>(sh.bits, sh.hist, nwords, sh.w0);
-        for (uint32_t i = tid; i < C; i += THREADS) {
-          const v2u e = sh.cand[i];
-          if ((sh.bits[e.y >> 5] >> (e.y & 31)) & 1u) emit(bitmap_rank(sh.bits, sh.hist, e.y), e.y, e.x);
+        if (kChunks == 1) {
+          // The list lives in registers now: stage the output row in its LDS
+          // and store the row with coalesced writes.
+          v2u* stage = sh.cand;
+#pragma unroll
+          for (int j = 0; j < kRegPairs; ++j) {
+            const uint32_t pos = reg[j].y;
+            if (reg[j].x != 0u && ((sh.bits[pos >> 5] >> (pos & 31)) & 1u))
+              stage[bitmap_rank(sh.bits, sh.hist, pos)] = reg[j];
+          }
+          __syncthreads();
+          for (int o = tid; o < a.k; o += THREADS) {
+            if (o < (int)kk) {
+              const v2u e = stage[o];
+              emit((uint32_t)o, e.y, e.x);
+            } else if (FINAL) {
+              a.out[out_base + o] = -1;
+            } else {
+              a.out_keys[out_base + o] = 0u;
+              a.out_idx[out_base + o] = -1;
+            }
+          }
+          row_written = true;
+        } else {
+          for (int ch = 0; ch < kChunks; ++ch) {
+            load_chunk(ch);
+#pragma unroll
+            for (int j = 0; j < kRegPairs; ++j) {
+              const uint32_t pos = reg[j].y;
+              if (reg[j].x != 0u && ((sh.bits[pos >> 5] >> (pos & 31)) & 1u))
+                emit(bitmap_rank(sh.bits, sh.hist, pos), pos, reg[j].x);
+            }
+          }
         }
         done = true;
       }
@@ -690,12 +745,14 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
     }
   }
   // padding after the kk selected entries
-  for (int o = (int)kk + tid; o < a.k; o += THREADS) {
-    if (FINAL) {
-      a.out[out_base + o] = -1;
-    } else {
-      a.out_keys[out_base + o] = 0u;
-      a.out_idx[out_base + o] = -1;
+  if (!row_written) {
+    for (int o = (int)kk + tid; o < a.k; o += THREADS) {
+      if (FINAL) {
+        a.out[out_base + o] = -1;
+      } else {
+        a.out_keys[out_base + o] = 0u;
+        a.out_idx[out_base + o] = -1;
+      }
     }
   }
 }
