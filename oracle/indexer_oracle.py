@@ -122,6 +122,40 @@ def encode_e4m3fn(x: np.ndarray, saturate: bool = True) -> np.ndarray:
     return out
 
 
+E4M3_MAX = 448.0
+
+
+def quant_fp8_rows(x: np.ndarray):
+    """Per-row e4m3fn quantisation: (codes uint8 [rows, D], scale float32 [rows]).
+
+    This is the step that produces the path's fp8 inputs: kv codes with their
+    per-token kv_scale, and q codes (per row and head).  The PR #87 page
+    names an ``act_quant`` kernel and pins the e4m3fn encoder (ties to even,
+    subnormals, saturation to +-448, NaN); it does not print the scale rule,
+    so this takes the plainest reading that makes the largest magnitude of a
+    row land on the largest finite code:
+
+        amax  = max_d |x[r, d]|            (a row of zeros takes amax = 448)
+        inv   = float32(448 / amax)        one float32 division
+        y     = float32(x[r, d] * inv)     one float32 multiply
+        codes = e4m3fn(y)                  nearest, ties to even, saturating
+        scale = float32(amax / 448)        so that x ~ decode(code) * scale
+
+    The code is decided in float32 (the precision the GPU kernel computes y
+    in), so both sides round the same float32 y.  Inputs must be finite.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    if x.ndim != 2:
+        raise ValueError("x must be [rows, D]")
+    amax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    amax = np.where(amax > 0, amax, np.float32(E4M3_MAX)).astype(np.float32)
+    inv = (np.float32(E4M3_MAX) / amax).astype(np.float32)
+    y = (x * inv[:, None]).astype(np.float32)
+    codes = encode_e4m3fn(y.astype(np.float64))
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    return codes, scale
+
+
 def _round_half_even(u: float) -> int:
     fl = math.floor(u)
     r = u - fl
