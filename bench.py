@@ -59,6 +59,7 @@ def _args():
     ap.add_argument("--fused-check", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--all-workloads", default="")
+    ap.add_argument("--quant", action="store_true", help="time the fp8 quantiser on the path's kv and q shapes")
     return ap.parse_args()
 
 
@@ -279,6 +280,44 @@ def run_workload(name, steps, warmup, fused_check):
     return res
 
 
+QUANT_SHAPES = (
+    ("kv_n65536_d128", 65536, 128),          # the 65536-key prefill's kv (per-token scales)
+    ("q_m8192_h32_d128", 8192 * 32, 128),    # its q, one row per (query row, head)
+    ("kv_n210000_d128", 210000, 128),        # the long-prefix workload's kv
+)
+
+
+def quant_workloads(steps, warmup):
+    """Time indexer_quant_fp8 on the path's kv and q shapes: HBM bytes = 4 read + 1 written per
+    element plus 4 per row (the scale), HIP events on the launch stream around each launch."""
+    import torch
+    import fp8_mqa_logits_amd as F
+    from workloads.generate import quant_inputs
+    out = []
+    for name, rows, D in QUANT_SHAPES:
+        x = torch.from_numpy(quant_inputs(rows, D, seed=rows)).cuda()
+        codes = torch.empty((rows, D), dtype=torch.uint8, device="cuda")
+        scale = torch.empty(rows, dtype=torch.float32, device="cuda")
+        for _ in range(warmup):
+            F.indexer_quant_fp8(x, codes=codes, scale=scale)
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            F.indexer_quant_fp8(x, codes=codes, scale=scale)
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+        nbytes = rows * D * 5 + rows * 4
+        out.append({"workload": f"quant_{name}", "rows": rows, "D": D, "ms": ms, "hbm_bytes": nbytes,
+                    "gbps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / HBM_PEAK})
+        del x, codes, scale
+        torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration():
     import torch
     nbytes = 1 << 30
@@ -320,8 +359,15 @@ def main():
             print(json.dumps(r), file=sys.stderr, flush=True)
             del inp, step
             torch.cuda.empty_cache()
+        for q in quant_workloads(a.steps, a.warmup):
+            rows.append(q)
+            print(json.dumps(q), file=sys.stderr, flush=True)
         with open(a.all_workloads, "w") as f:
             json.dump(rows, f, indent=1)
+        return
+    if a.quant:
+        for q in quant_workloads(a.steps, a.warmup):
+            print(json.dumps(q), flush=True)
         return
 
     r = run_workload(a.workload, a.steps, a.warmup, a.fused_check)

@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     indexer_topk,
     indexer_logits_topk_ragged,
     indexer_logits_topk_paged,
+    indexer_quant_fp8,
     fp8idx_workspace_bytes,
     fp8idx_workspace_bytes_paged,
     fp8idx_rows_per_chunk,

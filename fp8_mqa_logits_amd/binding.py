@@ -33,6 +33,7 @@ EXPORTED = (
     "indexer_logits_topk_ragged", "indexer_logits_topk_paged",
     "fp8idx_workspace_bytes", "fp8idx_workspace_bytes_paged", "fp8idx_rows_per_chunk",
     "fp8idx_status_string", "fp8idx_last_hip_error", "fp8idx_version",
+    "indexer_quant_fp8",
 )
 
 
@@ -88,6 +89,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fp8idx_status_string": (ctypes.c_char_p, [_I32]),
         "fp8idx_last_hip_error": (_I32, []),
         "fp8idx_version": (ctypes.c_char_p, []),
+        "indexer_quant_fp8": (_I32, [_P, _I64, _I64, _I32, _P, _I64, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -351,3 +353,30 @@ def indexer_logits_topk_paged(q, kv_pool, scale_pool, weights, row_len, block_ta
             int(bool(map_to_slots)), _ptr(out), out.shape[1], logits_cap_bytes, wp, wb, _stream(dev, stream))
     _check("indexer_logits_topk_paged", st)
     return out
+
+
+def indexer_quant_fp8(x, *, codes: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
+                      stream=None):
+    """Per-row e4m3fn quantisation of float32 x [rows, D] (or [..., D], flattened to rows).
+
+    Returns (codes uint8 [rows, D], scale float32 [rows]) with x ~ decode(codes) * scale.
+    """
+    dev = _dev(x, "x")
+    _need(x, "x", _F32, dev)
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    if codes is None:
+        codes = torch.empty((rows, D), dtype=torch.uint8, device=dev)
+    else:
+        codes = _fp8(codes, "codes", dev)
+    if scale is None:
+        scale = torch.empty((rows,), dtype=torch.float32, device=dev)
+    else:
+        _need(scale, "scale", _F32, dev)
+    if codes.numel() != rows * D or scale.numel() != rows:
+        raise ValueError("codes must hold rows * D bytes and scale rows floats")
+    L = load_library()
+    with torch.cuda.device(dev):
+        st = L.indexer_quant_fp8(_ptr(x), D, rows, D, _ptr(codes), D, _ptr(scale), _stream(dev, stream))
+    _check("indexer_quant_fp8", st)
+    return codes.view(rows, D), scale

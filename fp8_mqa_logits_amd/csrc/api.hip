@@ -187,6 +187,21 @@ size_t fp8idx_workspace_bytes(int32_t op, int32_t rows, int64_t width, int32_t k
   }
 }
 
+fp8idx_status indexer_quant_fp8(const float* x, int64_t ld_x, int64_t rows, int32_t D, uint8_t* codes,
+                                int64_t ld_codes, float* scale, void* stream) {
+  if (D < 4 || D > 2048 || D % 4 != 0) return FP8IDX_EUNSUPPORTED;
+  if (rows < 0) return FP8IDX_EINVAL;
+  if (rows == 0) return FP8IDX_OK;
+  if (!x || !codes || !scale) return FP8IDX_EINVAL;
+  if (!aligned(x, 16) || ld_x < D || ld_x % 4 != 0) return FP8IDX_EINVAL;
+  if (!aligned(codes, 4) || ld_codes < D || ld_codes % 4 != 0 || !aligned(scale, 4)) return FP8IDX_EINVAL;
+  DeviceInfo dev;
+  if (fp8idx_status s = current_device(&dev)) return s;
+  fp8idx::QuantArgs a{x, ld_x, rows, D, codes, ld_codes, scale};
+  const hipError_t e = fp8idx::launch_quant_fp8(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8IDX_OK : hip_fail(e);
+}
+
 fp8idx_status indexer_logits_ragged(const uint8_t* q, const uint8_t* kv, const float* kv_scale,
                                     const float* weights, const int32_t* ks, const int32_t* ke,
                                     int32_t m, int32_t n, int32_t H, int32_t D,

@@ -96,6 +96,16 @@ size_t topk_workspace_bytes(const TopkPlan& p);
 
 hipError_t launch_logits_ragged(const RaggedLogitsArgs& a, const DeviceInfo& dev, hipStream_t s);
 hipError_t launch_logits_paged(const PagedLogitsArgs& a, const DeviceInfo& dev, hipStream_t s);
+struct QuantArgs {
+  const float* x;
+  int64_t ld_x;
+  int64_t rows;
+  int32_t D;
+  uint8_t* codes;
+  int64_t ld_codes;
+  float* scale;
+};
+hipError_t launch_quant_fp8(const QuantArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, const TopkPlan& plan, void* ws, hipStream_t s);
 
 }  // namespace fp8idx

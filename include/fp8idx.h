@@ -210,6 +210,28 @@ FP8IDX_API fp8idx_status indexer_logits_topk_paged(const uint8_t* q, const uint8
                                         size_t logits_cap_bytes, void* ws, size_t ws_bytes,
                                         void* stream);
 
+/*
+ * Per-row fp8 e4m3fn quantisation (the `act_quant` step named on the
+ * vessl-ai/sglang PR #87 page, which also pins its encoder: nearest with
+ * ties to even, subnormals, saturation to +-448).  It produces this path's
+ * fp8 inputs: kv codes with the per-token kv_scale, or q codes (one row per
+ * query row and head).  For each row r:
+ *
+ *   amax     = max_d |x[r, d]|   (a row of zeros takes amax = 448)
+ *   codes[r, d] = e4m3fn(float32(x[r, d] * float32(448 / amax)))
+ *   scale[r] = float32(amax / 448)            so x ~ decode(code) * scale
+ *
+ *   x      [rows, ld_x] float32, ld_x >= D, ld_x % 4 == 0, 16-byte aligned
+ *   codes  [rows, ld_codes] uint8 output, ld_codes >= D, ld_codes % 4 == 0,
+ *          4-byte aligned; columns [0, D) are written
+ *   scale  [rows] float32 output
+ * 4 <= D <= 2048 with D % 4 == 0 (else FP8IDX_EUNSUPPORTED).  Inputs must be
+ * finite, with every nonzero row's amax at least 2^-100.  rows == 0 is a
+ * no-op.  Allocates nothing; runs on `stream`.
+ */
+FP8IDX_API fp8idx_status indexer_quant_fp8(const float* x, int64_t ld_x, int64_t rows, int32_t D,
+                                           uint8_t* codes, int64_t ld_codes, float* scale, void* stream);
+
 /* Bytes of device workspace an operation needs (0 when it needs none).
  * rows = logits rows (m or B * next_n), width = keys per row (n or the
  * paged width).  Pure host arithmetic. */

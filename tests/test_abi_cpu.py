@@ -34,7 +34,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.EXPORTED) == names
@@ -156,3 +156,18 @@ def test_fused_workspace_covers_chunk_and_candidates(lib):
     assert ws <= logits + cand + 4096
     # one-shot on 8192 x 65536: the full 2 GiB buffer, single-segment top-k
     assert F.fp8idx_workspace_bytes(F.OP_LOGITS_TOPK_RAGGED, 8192, 65536, 2048, 0) == 8192 * 65536 * 4
+
+
+def test_quant_validation(lib):
+    f = lib.indexer_quant_fp8
+    assert f(P, 128, 4, 130, P, 132, P, None) == EUNSUP      # D % 4 != 0
+    assert f(P, 4096, 4, 4096, P, 4096, P, None) == EUNSUP   # D > 2048
+    assert f(P, 128, -1, 128, P, 128, P, None) == EINVAL
+    assert f(NULL, 128, 0, 128, NULL, 128, NULL, None) == OK  # empty call is a no-op
+    assert f(NULL, 128, 4, 128, P, 128, P, None) == EINVAL
+    assert f(P + 4, 128, 4, 128, P, 128, P, None) == EINVAL  # x rows are read as 16-byte vectors
+    assert f(P, 126, 4, 128, P, 128, P, None) == EINVAL      # ld_x < D
+    assert f(P, 130, 4, 128, P, 128, P, None) == EINVAL      # ld_x % 4 != 0
+    assert f(P, 128, 4, 128, P + 2, 128, P, None) == EINVAL  # codes written as 4-byte words
+    assert f(P, 128, 4, 128, P, 130, P, None) == EINVAL
+    assert f(P, 128, 4, 128, P, 128, P, None) == EDEV

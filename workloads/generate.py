@@ -237,6 +237,15 @@ def paged_inputs(B: int, next_n: int, ctx_lo: int, ctx_hi: int, k: int, seed: in
 
 
 # The five synthetic workloads.  Seeds are the workload's ordinal.
+def quant_inputs(rows: int, D: int, seed: int, *, spread: float = 3.0) -> np.ndarray:
+    """float32 [rows, D] activations for the fp8 quantiser: randn per element times a
+    per-row magnitude 10**U[-spread, spread), so row scales span many octaves."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    x = torch.randn(rows, D, generator=g, dtype=torch.float32)
+    mag = torch.pow(10.0, (torch.rand(rows, 1, generator=g) * 2.0 - 1.0) * spread)
+    return (x * mag).to(torch.float32).numpy()
+
+
 def _tiny() -> RaggedInputs:
     return ragged_inputs(64, 4096, 512, seed=1, name="tiny_ragged_m64_n4096")
 
