@@ -59,6 +59,7 @@ def _args():
     ap.add_argument("--fused-check", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--all-workloads", default="")
+    ap.add_argument("--overlap", action="store_true", help="time the fused loop serial vs overlapped")
     ap.add_argument("--quant", action="store_true", help="time the fp8 quantiser on the path's kv and q shapes")
     return ap.parse_args()
 
@@ -120,6 +121,18 @@ class RaggedStep:
             self.fused_ws = torch.empty(self.fused_ws_bytes + 256, dtype=torch.uint8, device="cuda")
         self.F.indexer_logits_topk_ragged(self.q, self.kv, self.sc, self.w, self.ks, self.ke, self.inp.k,
                                           logits_cap_bytes=self.cap, out=self.out, workspace=self.fused_ws)
+
+    def run_overlap(self):
+        """The fused loop with chunk N - 1's top-k on a side stream while chunk N's logits run."""
+        import torch
+        if getattr(self, "overlap_ws", None) is None:
+            need = self.F.fp8idx_workspace_bytes(self.F.OP_LOGITS_TOPK_RAGGED_OVERLAP, self.inp.m, self.inp.n,
+                                                 self.inp.k, self.cap)
+            self.overlap_ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+            self.side = torch.cuda.Stream()
+        self.F.indexer_logits_topk_ragged_overlap(self.q, self.kv, self.sc, self.w, self.ks, self.ke, self.inp.k,
+                                                  side_stream=self.side, logits_cap_bytes=self.cap,
+                                                  out=self.out, workspace=self.overlap_ws)
 
     def kernel_times(self):
         """Average logits and top-k launch durations (ms) over the recorded launches."""
@@ -206,14 +219,15 @@ def _time_steps(step, steps, warmup, record):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def _time_fused(step, steps, warmup):
+def _time_fused(step, steps, warmup, overlap=False):
     import torch
+    run = step.run_overlap if overlap else step.run_fused
     for _ in range(warmup):
-        step.run_fused()
+        run()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step.run_fused()
+        run()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / steps
 
@@ -277,6 +291,8 @@ def run_workload(name, steps, warmup, fused_check):
            "launches_per_step": per_step, "flops": step.flops(), "inp": inp, "step": step}
     if fused_check:
         res["fused_ms_per_step"] = _time_fused(step, steps, warmup)
+        if hasattr(step, "run_overlap") and step.rpc < inp.m:
+            res["overlap_ms_per_step"] = _time_fused(step, steps, warmup, overlap=True)
     return res
 
 
@@ -364,6 +380,22 @@ def main():
             print(json.dumps(q), file=sys.stderr, flush=True)
         with open(a.all_workloads, "w") as f:
             json.dump(rows, f, indent=1)
+        return
+    if a.overlap:
+        from workloads.generate import config_inputs
+        for name, cap in (("prefill_64k", 2_000_000_000), ("long_prefix_210k", None)):
+            inp = config_inputs(name)
+            if cap is not None:
+                inp.cap_bytes = cap
+                inp.name = f"{inp.name}_cap2GB"
+            step = RaggedStep(inp)
+            serial = _time_fused(step, a.steps, a.warmup)
+            over = _time_fused(step, a.steps, a.warmup, overlap=True)
+            print(json.dumps({"workload": inp.name, "chunks": -(-inp.m // step.rpc), "rows_per_chunk": step.rpc,
+                              "fused_serial_ms": round(serial, 4), "fused_overlap_ms": round(over, 4),
+                              "overlap_gain": round(serial / over - 1, 4)}), flush=True)
+            del step, inp
+            torch.cuda.empty_cache()
         return
     if a.quant:
         for q in quant_workloads(a.steps, a.warmup):

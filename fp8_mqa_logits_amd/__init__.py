@@ -13,12 +13,14 @@ from .binding import (  # noqa: F401
     MAP_BLOCK_TABLE,
     OP_TOPK,
     OP_LOGITS_TOPK_RAGGED,
+    OP_LOGITS_TOPK_RAGGED_OVERLAP,
     LIB_PATH,
     load_library,
     indexer_logits_ragged,
     indexer_logits_paged,
     indexer_topk,
     indexer_logits_topk_ragged,
+    indexer_logits_topk_ragged_overlap,
     indexer_logits_topk_paged,
     indexer_quant_fp8,
     fp8idx_workspace_bytes,

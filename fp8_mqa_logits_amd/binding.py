@@ -26,14 +26,14 @@ D = 128
 
 STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "EDEVICE", 5: "EHIP"}
 MAP_NONE, MAP_TOKEN_TABLE, MAP_BLOCK_TABLE = 0, 1, 2
-OP_TOPK, OP_LOGITS_TOPK_RAGGED = 0, 1
+OP_TOPK, OP_LOGITS_TOPK_RAGGED, OP_LOGITS_TOPK_RAGGED_OVERLAP = 0, 1, 2
 
 EXPORTED = (
     "indexer_logits_ragged", "indexer_logits_paged", "indexer_topk",
     "indexer_logits_topk_ragged", "indexer_logits_topk_paged",
     "fp8idx_workspace_bytes", "fp8idx_workspace_bytes_paged", "fp8idx_rows_per_chunk",
     "fp8idx_status_string", "fp8idx_last_hip_error", "fp8idx_version",
-    "indexer_quant_fp8",
+    "indexer_quant_fp8", "indexer_logits_topk_ragged_overlap",
 )
 
 
@@ -90,6 +90,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fp8idx_last_hip_error": (_I32, []),
         "fp8idx_version": (ctypes.c_char_p, []),
         "indexer_quant_fp8": (_I32, [_P, _I64, _I64, _I32, _P, _I64, _P, _P]),
+        "indexer_logits_topk_ragged_overlap": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                                      ctypes.POINTER(_CMap), _P, _I64, _SZ, _P, _SZ, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -321,6 +323,37 @@ def indexer_logits_topk_ragged(q, kv, kv_scale, weights, ks, ke, k: int, *,
             _ptr(q8), _ptr(kv8), _ptr(kv_scale), _ptr(weights), _ptr(ks), _ptr(ke), m, n, H, D, k,
             _cmap(map), _ptr(out), out.shape[1], logits_cap_bytes, wp, wb, _stream(dev, stream))
     _check("indexer_logits_topk_ragged", st)
+    return out
+
+
+def indexer_logits_topk_ragged_overlap(q, kv, kv_scale, weights, ks, ke, k: int, *, side_stream,
+                                       map: Optional[TopkMap] = None, logits_cap_bytes: int = 0,
+                                       out: Optional[torch.Tensor] = None,
+                                       workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """indexer_logits_topk_ragged with chunk N - 1's top-k on ``side_stream`` while chunk N's logits run."""
+    dev = _dev(q, "q")
+    q8 = _fp8(q, "q", dev)
+    kv8 = _fp8(kv, "kv", dev)
+    m, n = q8.shape[0], kv8.shape[0]
+    if q8.shape[1:] != (H, D) or kv8.shape[1:] != (D,):
+        raise ValueError("q must be [m, 32, 128] and kv [n, 128]")
+    _need(kv_scale, "kv_scale", _F32, dev)
+    _need(weights, "weights", _F32, dev)
+    _need(ks, "ks", _I32T, dev)
+    _need(ke, "ke", _I32T, dev)
+    if out is None:
+        out = torch.empty((m, k), dtype=torch.int32, device=dev)
+    else:
+        _need(out, "out", _I32T, dev)
+    L = load_library()
+    need = int(L.fp8idx_workspace_bytes(OP_LOGITS_TOPK_RAGGED_OVERLAP, m, n, k, logits_cap_bytes))
+    wp, wb = _workspace(need, dev, workspace)
+    with torch.cuda.device(dev):
+        st = L.indexer_logits_topk_ragged_overlap(
+            _ptr(q8), _ptr(kv8), _ptr(kv_scale), _ptr(weights), _ptr(ks), _ptr(ke), m, n, H, D, k,
+            _cmap(map), _ptr(out), out.shape[1], logits_cap_bytes, wp, wb, _stream(dev, stream),
+            _stream(dev, side_stream))
+    _check("indexer_logits_topk_ragged_overlap", st)
     return out
 
 

@@ -138,14 +138,34 @@ fp8idx_status check_topk_args(int32_t rows, int32_t width, int64_t ld, int32_t k
   return FP8IDX_OK;
 }
 
-size_t fused_ws_bytes(int32_t rows, int64_t width, int32_t k, size_t cap, int32_t granule) {
+// Events of the overlapped fused entry, created once per device: [0..1] a
+// chunk buffer's logits are written, [2..3] its top-k has read them.
+std::once_flag g_ev_once[kMaxDevices];
+hipEvent_t g_ev[kMaxDevices][4];
+int g_ev_ok[kMaxDevices];
+
+fp8idx_status overlap_events(hipEvent_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8IDX_EDEVICE;
+  std::call_once(g_ev_once[dev], [dev]() {
+    g_ev_ok[dev] = 1;
+    for (int i = 0; i < 4; ++i)
+      if (hipEventCreateWithFlags(&g_ev[dev][i], hipEventDisableTiming) != hipSuccess) g_ev_ok[dev] = 0;
+  });
+  if (!g_ev_ok[dev]) return FP8IDX_EHIP;
+  *out = g_ev[dev];
+  return FP8IDX_OK;
+}
+
+size_t fused_ws_bytes(int32_t rows, int64_t width, int32_t k, size_t cap, int32_t granule,
+                      int32_t logit_buffers = 1) {
   const int64_t ld = ws_logits_ld(width);
   int32_t rpc = rows_per_chunk(cap, ld, rows);
   if (granule > 1 && rpc < rows) rpc = std::max<int32_t>(granule, rpc / granule * granule);
   rpc = std::min(rpc, rows);
   if (rpc <= 0) return 0;
   const int32_t last = rows % rpc == 0 ? rpc : rows % rpc;
-  const size_t logits = align256((size_t)rpc * (size_t)ld * 4u);
+  const size_t logits = align256((size_t)rpc * (size_t)ld * 4u) * (size_t)(rpc < rows ? logit_buffers : 1);
   const size_t t0 = fp8idx::topk_workspace_bytes(fp8idx::plan_topk(rpc, width, k));
   const size_t t1 = fp8idx::topk_workspace_bytes(fp8idx::plan_topk(last, width, k));
   return logits + std::max(t0, t1);
@@ -182,6 +202,8 @@ size_t fp8idx_workspace_bytes(int32_t op, int32_t rows, int64_t width, int32_t k
       return fp8idx::topk_workspace_bytes(fp8idx::plan_topk(rows, width, k));
     case FP8IDX_OP_LOGITS_TOPK_RAGGED:
       return fused_ws_bytes(rows, width, k, logits_cap_bytes, 1);
+    case FP8IDX_OP_LOGITS_TOPK_RAGGED_OVERLAP:
+      return fused_ws_bytes(rows, width, k, logits_cap_bytes, 1, 2);
     default:
       return 0;
   }
@@ -286,6 +308,58 @@ fp8idx_status indexer_logits_topk_ragged(const uint8_t* q, const uint8_t* kv, co
     e = fp8idx::launch_topk(ta, plan, topk_ws, st);
     if (e != hipSuccess) return hip_fail(e);
   }
+  return FP8IDX_OK;
+}
+
+fp8idx_status indexer_logits_topk_ragged_overlap(const uint8_t* q, const uint8_t* kv, const float* kv_scale,
+                                                 const float* weights, const int32_t* ks, const int32_t* ke,
+                                                 int32_t m, int32_t n, int32_t H, int32_t D, int32_t k,
+                                                 const fp8idx_map* map, int32_t* out, int64_t ld_out,
+                                                 size_t logits_cap_bytes, void* ws, size_t ws_bytes, void* stream,
+                                                 void* side_stream) {
+  if (fp8idx_status s = check_ragged(q, kv, kv_scale, weights, ks, ke, m, n, H, D)) return s;
+  if (fp8idx_status s = check_topk_args(m, n, n, k, ld_out)) return s;
+  if (fp8idx_status s = check_map(map)) return s;
+  if (m == 0) return FP8IDX_OK;
+  if (!out || !aligned(out, 4)) return FP8IDX_EINVAL;
+  if (side_stream == nullptr || side_stream == stream) return FP8IDX_EINVAL;
+  const size_t need = fused_ws_bytes(m, n, k, logits_cap_bytes, 1, 2);
+  if (ws == nullptr || ws_bytes < need) return FP8IDX_EWORKSPACE;
+  if (!aligned(ws, 256)) return FP8IDX_EINVAL;
+  DeviceInfo dev;
+  if (fp8idx_status s = current_device(&dev)) return s;
+  hipEvent_t* ev = nullptr;
+  if (fp8idx_status s = overlap_events(&ev)) return s;
+
+  const hipStream_t main_st = static_cast<hipStream_t>(stream);
+  const hipStream_t side = static_cast<hipStream_t>(side_stream);
+  const int64_t ld = ws_logits_ld(n);
+  const int32_t rpc = rows_per_chunk(logits_cap_bytes, ld, m);
+  const int32_t nchunks = (m + rpc - 1) / rpc;
+  const size_t buf_bytes = align256((size_t)rpc * (size_t)ld * 4u);
+  float* bufs[2] = {static_cast<float*>(ws),
+                    reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + (nchunks > 1 ? buf_bytes : 0))};
+  void* topk_ws = static_cast<uint8_t*>(ws) + buf_bytes * (nchunks > 1 ? 2 : 1);
+  const fp8idx::TopkMap kmap = to_kernel_map(map);
+  hipError_t e = hipSuccess;
+  for (int32_t c = 0; c < nchunks; ++c) {
+    const int32_t s0 = c * rpc;
+    const int32_t rows = std::min(rpc, m - s0);
+    const int b = c & 1;
+    // the top-k of chunk c - 2 must have read this buffer before it is rewritten
+    if (c >= 2 && (e = hipStreamWaitEvent(main_st, ev[2 + b], 0)) != hipSuccess) return hip_fail(e);
+    fp8idx::RaggedLogitsArgs la{q + (size_t)s0 * fp8idx::kQRowBytesHost, kv, kv_scale,
+                                weights + (size_t)s0 * 32, ks + s0, ke + s0, rows, n, bufs[b], ld, 0};
+    if ((e = fp8idx::launch_logits_ragged(la, dev, main_st)) != hipSuccess) return hip_fail(e);
+    if ((e = hipEventRecord(ev[b], main_st)) != hipSuccess) return hip_fail(e);
+    if ((e = hipStreamWaitEvent(side, ev[b], 0)) != hipSuccess) return hip_fail(e);
+    const fp8idx::TopkPlan plan = fp8idx::plan_topk(rows, n, k);
+    fp8idx::TopkArgs ta{bufs[b], ld, rows, n, ks + s0, ke + s0, k, s0, kmap, out + (int64_t)s0 * ld_out, ld_out};
+    if ((e = fp8idx::launch_topk(ta, plan, topk_ws, side)) != hipSuccess) return hip_fail(e);
+    if ((e = hipEventRecord(ev[2 + b], side)) != hipSuccess) return hip_fail(e);
+  }
+  // join: the side stream runs the top-ks in order, so the last one implies all
+  if ((e = hipStreamWaitEvent(main_st, ev[2 + ((nchunks - 1) & 1)], 0)) != hipSuccess) return hip_fail(e);
   return FP8IDX_OK;
 }
 

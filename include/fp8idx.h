@@ -101,7 +101,8 @@ typedef struct fp8idx_map {
 /* Operation selector for fp8idx_workspace_bytes(). */
 typedef enum fp8idx_op {
   FP8IDX_OP_TOPK = 0,              /* indexer_topk */
-  FP8IDX_OP_LOGITS_TOPK_RAGGED = 1 /* indexer_logits_topk_ragged */
+  FP8IDX_OP_LOGITS_TOPK_RAGGED = 1, /* indexer_logits_topk_ragged */
+  FP8IDX_OP_LOGITS_TOPK_RAGGED_OVERLAP = 2 /* indexer_logits_topk_ragged_overlap */
 } fp8idx_op;
 
 /*
@@ -189,6 +190,33 @@ FP8IDX_API fp8idx_status indexer_logits_topk_ragged(const uint8_t* q, const uint
                                          int32_t* out, int64_t ld_out,
                                          size_t logits_cap_bytes, void* ws, size_t ws_bytes,
                                          void* stream);
+
+/*
+ * The same row-chunked loop with the top-k of chunk N - 1 running on
+ * `side_stream` while the logits of chunk N run on `stream` (the chunking
+ * page's `_run_chunked_pipelined`, which asks whether small chunks cost
+ * through serialisation or through small-M inefficiency).  Two chunk logits
+ * buffers alternate in the workspace; device events order each buffer's
+ * writes, its top-k read and its reuse, and `stream` waits for the last
+ * top-k before the call returns, so work enqueued on `stream` afterwards
+ * sees every output.  Output is identical to indexer_logits_topk_ragged.
+ *
+ *   side_stream   a stream other than `stream` (else FP8IDX_EINVAL)
+ *   ws_bytes      >= fp8idx_workspace_bytes(FP8IDX_OP_LOGITS_TOPK_RAGGED_OVERLAP,
+ *                    m, n, k, logits_cap_bytes)
+ * The entry keeps four events per device, created on its first call on that
+ * device; calls of this entry that overlap on one device race on them.
+ * Stream capture works as a fork (the side stream joins through the first
+ * event) and a join (the final wait).
+ */
+FP8IDX_API fp8idx_status indexer_logits_topk_ragged_overlap(const uint8_t* q, const uint8_t* kv,
+                                                 const float* kv_scale, const float* weights,
+                                                 const int32_t* ks, const int32_t* ke,
+                                                 int32_t m, int32_t n, int32_t H, int32_t D,
+                                                 int32_t k, const fp8idx_map* map,
+                                                 int32_t* out, int64_t ld_out,
+                                                 size_t logits_cap_bytes, void* ws, size_t ws_bytes,
+                                                 void* stream, void* side_stream);
 
 /*
  * Fused paged logits + top-k.  Output indices are physical kv slots

@@ -34,7 +34,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.EXPORTED) == names
@@ -171,3 +171,24 @@ def test_quant_validation(lib):
     assert f(P, 128, 4, 128, P + 2, 128, P, None) == EINVAL  # codes written as 4-byte words
     assert f(P, 128, 4, 128, P, 130, P, None) == EINVAL
     assert f(P, 128, 4, 128, P, 128, P, None) == EDEV
+
+
+def test_overlap_validation(lib):
+    f = lib.indexer_logits_topk_ragged_overlap
+    S1, S2 = P, P + 4096                                  # two distinct fake stream handles
+    cap = 4 * 1000 * 4                                    # 4 rows per chunk: chunks of 4, 4, 2 rows
+    args = [P, P, P, P, P, P, 10, 1000, 32, 128, 64, None, P, 64, cap, None, 0, S1, S2]
+    need = lib.fp8idx_workspace_bytes(binding.OP_LOGITS_TOPK_RAGGED_OVERLAP, 10, 1000, 64, cap)
+    one = lib.fp8idx_workspace_bytes(binding.OP_LOGITS_TOPK_RAGGED, 10, 1000, 64, cap)
+    # two chunk buffers (each 16000 bytes rounded up to 256) instead of one
+    assert need == one + 16128
+    assert f(*args) == EWS
+    args[15], args[16] = P, need
+    bad = list(args); bad[18] = S1
+    assert f(*bad) == EINVAL                              # side stream must differ from the stream
+    bad = list(args); bad[18] = None
+    assert f(*bad) == EINVAL
+    assert f(*args) == EDEV
+    # one chunk needs only one buffer
+    assert lib.fp8idx_workspace_bytes(binding.OP_LOGITS_TOPK_RAGGED_OVERLAP, 10, 1000, 64, 0) == \
+        lib.fp8idx_workspace_bytes(binding.OP_LOGITS_TOPK_RAGGED, 10, 1000, 64, 0)

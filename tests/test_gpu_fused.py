@@ -168,3 +168,57 @@ def test_two_streams_concurrently():
     torch.cuda.synchronize()
     for oa, ob in outs:
         assert torch.equal(oa, ref_a) and torch.equal(ob, ref_b)
+
+
+@pytest.mark.parametrize("cap_rows", [0, 1, 7, 16, 23])
+def test_overlap_equals_serial_bytes(cap_rows):
+    inp = ragged_inputs(61, 2500, 100, seed=41)
+    d = _dev(inp)
+    ld = (inp.n + 3) // 4 * 4
+    cap = cap_rows * ld * 4
+    ref = F.indexer_logits_topk_ragged(*d, 100, logits_cap_bytes=cap)
+    side = torch.cuda.Stream()
+    got = F.indexer_logits_topk_ragged_overlap(*d, 100, side_stream=side, logits_cap_bytes=cap)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, got)
+
+
+def test_overlap_token_table_and_back_to_back_calls():
+    inp = multi_request_ragged([(700, 9), (1500, 30), (90, 5)], k=64, seed=42)
+    d = _dev(inp)
+    m = F.TopkMap(kind=F.MAP_TOKEN_TABLE, table=to_dev(inp.table), cu_rows=to_dev(inp.cu_rows))
+    ld = (inp.n + 3) // 4 * 4
+    cap = 11 * ld * 4
+    ref = F.indexer_logits_topk_ragged(*d, inp.k, map=m, logits_cap_bytes=cap)
+    need = F.fp8idx_workspace_bytes(F.OP_LOGITS_TOPK_RAGGED_OVERLAP, inp.m, inp.n, inp.k, cap)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    outs = [F.indexer_logits_topk_ragged_overlap(*d, inp.k, side_stream=side, map=m, logits_cap_bytes=cap,
+                                                 workspace=ws) for _ in range(4)]
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, ref)
+
+
+def test_overlap_graph_replay():
+    inp = ragged_inputs(300, 20000, 2048, seed=44)
+    d = _dev(inp)
+    ld = (inp.n + 3) // 4 * 4
+    cap = 64 * ld * 4
+    ref = F.indexer_logits_topk_ragged(*d, inp.k, logits_cap_bytes=cap)
+    need = F.fp8idx_workspace_bytes(F.OP_LOGITS_TOPK_RAGGED_OVERLAP, inp.m, inp.n, inp.k, cap)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    s, side = torch.cuda.Stream(), torch.cuda.Stream()
+    out_g = torch.full((inp.m, inp.k), -7, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            F.indexer_logits_topk_ragged_overlap(*d, inp.k, side_stream=side, logits_cap_bytes=cap, out=out_g,
+                                                 workspace=ws, stream=s)
+    for rep in range(3):
+        out_g.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, ref), f"graph replay {rep} differs from eager"
