@@ -342,6 +342,71 @@ def paged_topk_mapped(inp, rows: Optional[Sequence[int]] = None, width: Optional
     return L, raw, mapped
 
 
+# ---------------------------------------------------------------------------
+# Index preparation (the gen_nsa_ks_ke step on the lightllm PR pages)
+# ---------------------------------------------------------------------------
+
+def prepare_ragged(seq_len, q_len, req_idx, table):
+    """Ragged prefill indices for a batch of requests, written out one element at a time.
+
+    Request b holds seq_len[b] tokens whose last q_len[b] are this step's queries
+    (q_len is clamped to [0, seq_len]).  The keys of all requests are laid out
+    back to back (the ragged key space), request b's first at cu_seq[b]; its
+    token p is kv slot table[req_idx[b], p] (the req -> token table).
+
+    Returns a dict of int64 arrays:
+      cu_seq [B+1], cu_q [B+1]   prefix sums of the lengths
+      ks, ke [total_q]           query t of request b (global index cu_q[b] + t) sees
+                                 ragged keys [cu_seq[b], cu_seq[b] + seq_len[b] - q_len[b] + t + 1)
+      ragged_mem [total_seq]     ragged key cu_seq[b] + p -> table[req_idx[b], p]
+                                 (-1 when p lies past the table row or req_idx is out of range)
+    """
+    seq_len = [max(0, int(v)) for v in seq_len]
+    q_len = [min(max(0, int(v)), s) for v, s in zip(q_len, seq_len)]
+    table = np.asarray(table)
+    B = len(seq_len)
+    cu_seq = [0]
+    cu_q = [0]
+    for b in range(B):
+        cu_seq.append(cu_seq[-1] + seq_len[b])
+        cu_q.append(cu_q[-1] + q_len[b])
+    ks, ke, mem = [], [], []
+    for b in range(B):
+        for t in range(q_len[b]):
+            ks.append(cu_seq[b])
+            ke.append(cu_seq[b] + seq_len[b] - q_len[b] + t + 1)
+        r = int(req_idx[b])
+        for p in range(seq_len[b]):
+            ok = 0 <= r < table.shape[0] and p < table.shape[1]
+            mem.append(int(table[r, p]) if ok else -1)
+    as64 = lambda v: np.asarray(v, dtype=np.int64)
+    return {"cu_seq": as64(cu_seq), "cu_q": as64(cu_q), "ks": as64(ks), "ke": as64(ke), "ragged_mem": as64(mem)}
+
+
+def prepare_decode(seq_len, next_n, req_idx, req_to_page):
+    """Paged decode / MTP indices: request b's next_n query rows are its last next_n tokens.
+
+      row_len [B * next_n]          row t of request b sees keys [0, seq_len[b] - next_n + t + 1)
+                                    (at least 0)
+      block_table [B, max_pages]    row b is req_to_page[req_idx[b]] (-1 past the table or for
+                                    an out-of-range req_idx)
+    """
+    next_n = int(next_n)
+    req_to_page = np.asarray(req_to_page)
+    B = len(seq_len)
+    max_pages = req_to_page.shape[1]
+    row_len = []
+    bt = np.full((B, max_pages), -1, dtype=np.int64)
+    for b in range(B):
+        for t in range(next_n):
+            row_len.append(max(0, int(seq_len[b]) - next_n + t + 1))
+        r = int(req_idx[b])
+        if 0 <= r < req_to_page.shape[0]:
+            for p in range(max_pages):
+                bt[b, p] = int(req_to_page[r, p])
+    return {"row_len": np.asarray(row_len, dtype=np.int64), "block_table": bt}
+
+
 def rows_per_chunk(cap_bytes: int, row_stride_elems: int, rows: int) -> int:
     """Rows per chunk of the row-chunked loop: floor(cap / (stride * 4)), at least 1.
 
