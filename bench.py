@@ -60,6 +60,7 @@ def _args():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--all-workloads", default="")
     ap.add_argument("--overlap", action="store_true", help="time the fused loop serial vs overlapped")
+    ap.add_argument("--prep", action="store_true", help="time index preparation at the PR page's shapes")
     ap.add_argument("--quant", action="store_true", help="time the fp8 quantiser on the path's kv and q shapes")
     return ap.parse_args()
 
@@ -334,6 +335,75 @@ def quant_workloads(steps, warmup):
     return out
 
 
+def _event_ms(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+
+
+def _graph_ms(fn, calls=20, replays=10):
+    """Per-call device time of fn from a graph of `calls` captured calls, replayed (the PR page
+    times its index kernels from CUDA-graph samples, without host launch cost)."""
+    import torch
+    s = torch.cuda.Stream()
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(calls):
+                fn(stream=s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (calls * replays)
+
+
+def prep_workloads(steps, warmup):
+    """Index preparation at the shape of the PR page's index benchmark: 8 requests x 1M tokens
+    (16 queries per request for prefill; 1 and 4 rows per request for decode and MTP, page 64).
+    Per-call device time from graph replays; `steps` and `warmup` are unused here."""
+    import torch
+    import fp8_mqa_logits_amd as F
+    B, S = 8, 1 << 20
+    g = torch.Generator(device="cpu").manual_seed(21)
+    table = torch.randint(0, 1 << 30, (B, S), generator=g, dtype=torch.int32).cuda()
+    seq = torch.full((B,), S, dtype=torch.int32, device="cuda")
+    req = torch.randperm(B, generator=g).to(torch.int32).cuda()
+    q16 = torch.full((B,), 16, dtype=torch.int32, device="cuda")
+    r2p = torch.randint(0, 1 << 20, (B, S // 64), generator=g, dtype=torch.int32).cuda()
+    out = []
+    ms = _graph_ms(lambda stream=None: F.indexer_prepare_ragged(seq, q16, req, table, max_q=B * 16,
+                                                                max_keys=B * S, stream=stream))
+    nbytes = B * S * 8
+    out.append({"workload": "prep_prefill_8x1M_q16_with_ragged_copy", "ms": ms, "hbm_bytes": nbytes,
+                "gbps": nbytes / (ms * 1e-3) / 1e9})
+    ms = _graph_ms(lambda stream=None: F.indexer_prepare_ragged(seq, q16, req, table, max_q=B * 16, max_keys=0,
+                                                                ragged_mem=False, stream=stream))
+    out.append({"workload": "prep_prefill_8x1M_q16_windows_only", "ms": ms})
+    for nn in (1, 4):
+        ms = _graph_ms(lambda stream=None: F.indexer_prepare_decode(seq, req, r2p, nn, stream=stream))
+        out.append({"workload": f"prep_decode_8x1M_next_n{nn}", "ms": ms, "hbm_bytes": B * (S // 64) * 8})
+    del table, r2p
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration():
     import torch
     nbytes = 1 << 30
@@ -375,7 +445,7 @@ def main():
             print(json.dumps(r), file=sys.stderr, flush=True)
             del inp, step
             torch.cuda.empty_cache()
-        for q in quant_workloads(a.steps, a.warmup):
+        for q in quant_workloads(a.steps, a.warmup) + prep_workloads(a.steps, a.warmup):
             rows.append(q)
             print(json.dumps(q), file=sys.stderr, flush=True)
         with open(a.all_workloads, "w") as f:
@@ -396,6 +466,10 @@ def main():
                               "overlap_gain": round(serial / over - 1, 4)}), flush=True)
             del step, inp
             torch.cuda.empty_cache()
+        return
+    if a.prep:
+        for q in prep_workloads(a.steps, a.warmup):
+            print(json.dumps(q), flush=True)
         return
     if a.quant:
         for q in quant_workloads(a.steps, a.warmup):

@@ -23,6 +23,8 @@ from .binding import (  # noqa: F401
     indexer_logits_topk_ragged_overlap,
     indexer_logits_topk_paged,
     indexer_quant_fp8,
+    indexer_prepare_ragged,
+    indexer_prepare_decode,
     fp8idx_workspace_bytes,
     fp8idx_workspace_bytes_paged,
     fp8idx_rows_per_chunk,

@@ -34,6 +34,7 @@ EXPORTED = (
     "fp8idx_workspace_bytes", "fp8idx_workspace_bytes_paged", "fp8idx_rows_per_chunk",
     "fp8idx_status_string", "fp8idx_last_hip_error", "fp8idx_version",
     "indexer_quant_fp8", "indexer_logits_topk_ragged_overlap",
+    "indexer_prepare_ragged", "indexer_prepare_decode",
 )
 
 
@@ -90,6 +91,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fp8idx_last_hip_error": (_I32, []),
         "fp8idx_version": (ctypes.c_char_p, []),
         "indexer_quant_fp8": (_I32, [_P, _I64, _I64, _I32, _P, _I64, _P, _P]),
+        "indexer_prepare_ragged": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _P, _P, _P, _P, _I64, _P, _I64, _P]),
+        "indexer_prepare_decode": (_I32, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _I32, _P]),
         "indexer_logits_topk_ragged_overlap": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                                       ctypes.POINTER(_CMap), _P, _I64, _SZ, _P, _SZ, _P, _P]),
     }
@@ -413,3 +416,49 @@ def indexer_quant_fp8(x, *, codes: Optional[torch.Tensor] = None, scale: Optiona
         st = L.indexer_quant_fp8(_ptr(x), D, rows, D, _ptr(codes), D, _ptr(scale), _stream(dev, stream))
     _check("indexer_quant_fp8", st)
     return codes.view(rows, D), scale
+
+
+def indexer_prepare_ragged(seq_len, q_len, req_idx, table, *, max_q: int, max_keys: int = 0,
+                           ragged_mem: bool = True, stream=None):
+    """Ragged prefill index preparation -> dict(cu_seq, cu_q, ks, ke, ragged_mem) of int32 device tensors.
+
+    ks/ke hold max_q entries and ragged_mem max_keys entries; entries past the totals are left as allocated.
+    """
+    dev = _dev(seq_len, "seq_len")
+    for t, n in ((seq_len, "seq_len"), (q_len, "q_len"), (req_idx, "req_idx"), (table, "table")):
+        _need(t, n, _I32T, dev)
+    if table.dim() != 2:
+        raise ValueError("table must be [rows, ld] int32")
+    B = seq_len.numel()
+    out = {"cu_seq": torch.empty(B + 1, dtype=torch.int32, device=dev),
+           "cu_q": torch.empty(B + 1, dtype=torch.int32, device=dev),
+           "ks": torch.empty(max(max_q, 0), dtype=torch.int32, device=dev),
+           "ke": torch.empty(max(max_q, 0), dtype=torch.int32, device=dev),
+           "ragged_mem": torch.empty(max(max_keys, 0), dtype=torch.int32, device=dev) if ragged_mem else None}
+    L = load_library()
+    with torch.cuda.device(dev):
+        st = L.indexer_prepare_ragged(_ptr(seq_len), _ptr(q_len), _ptr(req_idx), _ptr(table), table.shape[1],
+                                      table.shape[0], B, _ptr(out["cu_seq"]), _ptr(out["cu_q"]), _ptr(out["ks"]),
+                                      _ptr(out["ke"]), max_q, _ptr(out["ragged_mem"]), max_keys,
+                                      _stream(dev, stream))
+    _check("indexer_prepare_ragged", st)
+    return out
+
+
+def indexer_prepare_decode(seq_len, req_idx, req_to_page, next_n: int, *, max_pages: Optional[int] = None,
+                           stream=None):
+    """Paged decode / MTP index preparation -> (row_len [B * next_n], block_table [B, max_pages]) int32."""
+    dev = _dev(seq_len, "seq_len")
+    for t, n in ((seq_len, "seq_len"), (req_idx, "req_idx"), (req_to_page, "req_to_page")):
+        _need(t, n, _I32T, dev)
+    B = seq_len.numel()
+    mp = req_to_page.shape[1] if max_pages is None else int(max_pages)
+    row_len = torch.empty(B * next_n, dtype=torch.int32, device=dev)
+    bt = torch.empty((B, mp), dtype=torch.int32, device=dev)
+    L = load_library()
+    with torch.cuda.device(dev):
+        st = L.indexer_prepare_decode(_ptr(seq_len), _ptr(req_idx), _ptr(req_to_page), req_to_page.shape[1],
+                                      req_to_page.shape[0], B, next_n, _ptr(row_len), _ptr(bt), mp,
+                                      _stream(dev, stream))
+    _check("indexer_prepare_decode", st)
+    return row_len, bt

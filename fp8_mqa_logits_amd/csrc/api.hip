@@ -209,6 +209,47 @@ size_t fp8idx_workspace_bytes(int32_t op, int32_t rows, int64_t width, int32_t k
   }
 }
 
+fp8idx_status indexer_prepare_ragged(const int32_t* seq_len, const int32_t* q_len, const int32_t* req_idx,
+                                     const int32_t* table, int64_t ld_table, int32_t num_table_rows, int32_t B,
+                                     int32_t* cu_seq, int32_t* cu_q, int32_t* ks, int32_t* ke, int64_t max_q,
+                                     int32_t* ragged_mem, int64_t max_keys, void* stream) {
+  if (B < 0 || max_q < 0 || max_keys < 0 || num_table_rows < 0) return FP8IDX_EINVAL;
+  if (B > fp8idx::kPrepMaxReq) return FP8IDX_EUNSUPPORTED;
+  if (B == 0) return FP8IDX_OK;
+  if (!seq_len || !q_len || !req_idx || !cu_seq || !cu_q) return FP8IDX_EINVAL;
+  if (max_q > 0 && (!ks || !ke)) return FP8IDX_EINVAL;
+  if (ragged_mem && (!table || ld_table < 1)) return FP8IDX_EINVAL;
+  for (const void* p : {(const void*)seq_len, (const void*)q_len, (const void*)req_idx, (const void*)cu_seq,
+                        (const void*)cu_q, (const void*)ks, (const void*)ke, (const void*)table,
+                        (const void*)ragged_mem})
+    if (p && !aligned(p, 4)) return FP8IDX_EINVAL;
+  DeviceInfo dev;
+  if (fp8idx_status s = current_device(&dev)) return s;
+  fp8idx::PrepRaggedArgs a{seq_len, q_len, req_idx, table, ld_table, num_table_rows, B, cu_seq, cu_q,
+                           ks, ke, max_q, ragged_mem, ragged_mem ? max_keys : 0};
+  const hipError_t e = fp8idx::launch_prep_ragged(a, dev, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8IDX_OK : hip_fail(e);
+}
+
+fp8idx_status indexer_prepare_decode(const int32_t* seq_len, const int32_t* req_idx, const int32_t* req_to_page,
+                                     int64_t ld_req_to_page, int32_t num_table_rows, int32_t B, int32_t next_n,
+                                     int32_t* row_len, int32_t* block_table, int32_t max_pages, void* stream) {
+  if (B < 0 || next_n < 1 || max_pages < 0 || num_table_rows < 0 || ld_req_to_page < max_pages)
+    return FP8IDX_EINVAL;
+  if ((int64_t)B * next_n > 0x7fffffffLL) return FP8IDX_EUNSUPPORTED;
+  if (B == 0) return FP8IDX_OK;
+  if (!seq_len || !req_idx || !row_len || (max_pages > 0 && (!req_to_page || !block_table))) return FP8IDX_EINVAL;
+  for (const void* p : {(const void*)seq_len, (const void*)req_idx, (const void*)req_to_page, (const void*)row_len,
+                        (const void*)block_table})
+    if (p && !aligned(p, 4)) return FP8IDX_EINVAL;
+  DeviceInfo dev;
+  if (fp8idx_status s = current_device(&dev)) return s;
+  fp8idx::PrepDecodeArgs a{seq_len, req_idx, req_to_page, ld_req_to_page, num_table_rows, B, next_n,
+                           row_len, block_table, max_pages, max_pages};
+  const hipError_t e = fp8idx::launch_prep_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8IDX_OK : hip_fail(e);
+}
+
 fp8idx_status indexer_quant_fp8(const float* x, int64_t ld_x, int64_t rows, int32_t D, uint8_t* codes,
                                 int64_t ld_codes, float* scale, void* stream) {
   if (D < 4 || D > 2048 || D % 4 != 0) return FP8IDX_EUNSUPPORTED;

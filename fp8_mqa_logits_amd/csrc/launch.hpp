@@ -96,6 +96,39 @@ size_t topk_workspace_bytes(const TopkPlan& p);
 
 hipError_t launch_logits_ragged(const RaggedLogitsArgs& a, const DeviceInfo& dev, hipStream_t s);
 hipError_t launch_logits_paged(const PagedLogitsArgs& a, const DeviceInfo& dev, hipStream_t s);
+constexpr int kPrepMaxReq = 4096;   // requests per index-preparation call
+struct PrepRaggedArgs {
+  const int32_t* seq_len;
+  const int32_t* q_len;
+  const int32_t* req_idx;
+  const int32_t* table;
+  int64_t ld_table;
+  int32_t num_rows;
+  int32_t B;
+  int32_t* cu_seq;
+  int32_t* cu_q;
+  int32_t* ks;
+  int32_t* ke;
+  int64_t max_q;
+  int32_t* ragged_mem;
+  int64_t max_keys;
+};
+struct PrepDecodeArgs {
+  const int32_t* seq_len;
+  const int32_t* req_idx;
+  const int32_t* req_to_page;
+  int64_t ld_r2p;
+  int32_t num_rows;
+  int32_t B;
+  int32_t next_n;
+  int32_t* row_len;
+  int32_t* block_table;
+  int64_t ld_bt;
+  int32_t max_pages;
+};
+hipError_t launch_prep_ragged(const PrepRaggedArgs& a, const DeviceInfo& dev, hipStream_t s);
+hipError_t launch_prep_decode(const PrepDecodeArgs& a, hipStream_t s);
+
 struct QuantArgs {
   const float* x;
   int64_t ld_x;

@@ -260,6 +260,50 @@ FP8IDX_API fp8idx_status indexer_logits_topk_paged(const uint8_t* q, const uint8
 FP8IDX_API fp8idx_status indexer_quant_fp8(const float* x, int64_t ld_x, int64_t rows, int32_t D,
                                            uint8_t* codes, int64_t ld_codes, float* scale, void* stream);
 
+/*
+ * Ragged prefill index preparation (the `gen_nsa_ks_ke` step on the lightllm
+ * "parallel NSA ragged index copies" PR page).  Request b holds seq_len[b]
+ * tokens whose last q_len[b] are this step's queries (q_len clamped to
+ * [0, seq_len]); the keys of all requests lie back to back in the ragged key
+ * space, request b's first at cu_seq[b]:
+ *
+ *   cu_seq [B+1], cu_q [B+1] int32   prefix sums of seq_len and q_len
+ *   ks, ke [max_q] int32             query t of request b, at cu_q[b] + t, sees ragged
+ *                                    keys [cu_seq[b], cu_seq[b] + seq_len[b] - q_len[b] + t + 1)
+ *   ragged_mem [max_keys] int32      ragged key cu_seq[b] + p -> table[req_idx[b], p], the
+ *                                    kv slot (-1 past the table row or for an out-of-range
+ *                                    req_idx); NULL skips the copy
+ *   table [num_table_rows, ld_table] int32, the request -> token-slot table
+ *
+ * ks/ke and ragged_mem are written up to the totals or the capacities
+ * (max_q, max_keys), whichever is smaller; nothing past the totals is
+ * touched.  The totals must stay below 2^31.  B <= 4096 (else
+ * FP8IDX_EUNSUPPORTED); B == 0 is a no-op.  One launch, no host
+ * synchronisation, graph capturable.  Allocates nothing.
+ */
+FP8IDX_API fp8idx_status indexer_prepare_ragged(const int32_t* seq_len, const int32_t* q_len,
+                                                const int32_t* req_idx, const int32_t* table,
+                                                int64_t ld_table, int32_t num_table_rows, int32_t B,
+                                                int32_t* cu_seq, int32_t* cu_q, int32_t* ks, int32_t* ke,
+                                                int64_t max_q, int32_t* ragged_mem, int64_t max_keys,
+                                                void* stream);
+
+/*
+ * Paged decode / MTP index preparation.  Request b's next_n query rows are
+ * its last next_n tokens:
+ *   row_len [B * next_n] int32       row t of request b sees keys
+ *                                    [0, max(0, seq_len[b] - next_n + t + 1))
+ *   block_table [B, max_pages] int32 row b = req_to_page[req_idx[b], 0:max_pages]
+ *                                    (-1 for an out-of-range req_idx)
+ *   req_to_page [num_table_rows, ld_req_to_page] int32, ld_req_to_page >= max_pages
+ * The outputs feed indexer_logits_paged / indexer_logits_topk_paged.
+ */
+FP8IDX_API fp8idx_status indexer_prepare_decode(const int32_t* seq_len, const int32_t* req_idx,
+                                                const int32_t* req_to_page, int64_t ld_req_to_page,
+                                                int32_t num_table_rows, int32_t B, int32_t next_n,
+                                                int32_t* row_len, int32_t* block_table, int32_t max_pages,
+                                                void* stream);
+
 /* Bytes of device workspace an operation needs (0 when it needs none).
  * rows = logits rows (m or B * next_n), width = keys per row (n or the
  * paged width).  Pure host arithmetic. */

@@ -34,7 +34,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.EXPORTED) == names
@@ -192,3 +192,33 @@ def test_overlap_validation(lib):
     # one chunk needs only one buffer
     assert lib.fp8idx_workspace_bytes(binding.OP_LOGITS_TOPK_RAGGED_OVERLAP, 10, 1000, 64, 0) == \
         lib.fp8idx_workspace_bytes(binding.OP_LOGITS_TOPK_RAGGED, 10, 1000, 64, 0)
+
+
+def test_prepare_validation(lib):
+    f = lib.indexer_prepare_ragged
+    #        seq q  req table ld rows B  cu_s cu_q ks ke max_q mem max_keys
+    ok = [P, P, P, P, 64, 4, 3, P, P, P, P, 10, P, 100, None]
+    assert f(*ok) == EDEV
+    bad = list(ok); bad[6] = 4097
+    assert f(*bad) == EUNSUP                               # more requests than one call scans
+    bad = list(ok); bad[6] = -1
+    assert f(*bad) == EINVAL
+    bad = list(ok); bad[9] = None
+    assert f(*bad) == EINVAL                               # ks needed when max_q > 0
+    bad = list(ok); bad[3] = None
+    assert f(*bad) == EINVAL                               # the copy needs the table
+    bad = list(ok); bad[3], bad[12] = None, None
+    assert f(*bad) == EDEV                                 # ... unless it is skipped
+    bad = list(ok); bad[7] = P + 2
+    assert f(*bad) == EINVAL
+    bad = list(ok); bad[6] = 0
+    assert f(*bad) == OK
+    g = lib.indexer_prepare_decode
+    okd = [P, P, P, 32, 4, 3, 4, P, P, 32, None]
+    assert g(*okd) == EDEV
+    bad = list(okd); bad[6] = 0
+    assert g(*bad) == EINVAL                               # next_n >= 1
+    bad = list(okd); bad[3] = 16
+    assert g(*bad) == EINVAL                               # table rows shorter than max_pages
+    bad = list(okd); bad[5] = 0
+    assert g(*bad) == OK
