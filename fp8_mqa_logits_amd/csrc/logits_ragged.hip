@@ -25,8 +25,10 @@
 //   lane ends with one finished (row, key) logit, which is scaled by
 //   kv_scale[j] (factored out of the head sum: valid because kv_scale >= 0)
 //   and stored.  The per-head scores never leave registers.
-// - Tiles outside the union of the workgroup's row windows are skipped; only
-//   the partially covered edge tile is masked element by element.
+// - Tiles outside the union of the workgroup's row windows are skipped.  A
+//   tile inside every window of a wave's 4 rows (the common case) stores its
+//   logits without masks, at fixed offsets from one per-tile row pointer; only
+//   the partially covered edge tiles are masked element by element.
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -39,7 +41,7 @@ namespace fp8idx {
 constexpr int kTileKeys = 64;
 
 template <int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 2) void logits_ragged_kernel(RaggedLogitsArgs a, int splits,
+__global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogitsArgs a, int splits,
                                                                        int keys_per_split, int items) {
   constexpr int kThreads = 64 * WAVES;
   constexpr int kRows = 4 * WAVES;
@@ -131,6 +133,18 @@ __global__ __launch_bounds__(64 * WAVES, 2) void logits_ragged_kernel(RaggedLogi
     const int my_ks = s_ks[my_r];
     const int my_ke = s_ke[my_r];
     float* __restrict__ out_row = a.logits + (int64_t)(row_ok ? my_row : 0) * a.ld;
+    // Keys every row of this wave keeps: tiles inside [w_lo, w_hi) store unmasked.
+    int w_lo = 0, w_hi = 0;
+    if (row0 + 4 * wave + 3 < a.m) {
+      w_lo = max(max(s_ks[4 * wave], s_ks[4 * wave + 1]), max(s_ks[4 * wave + 2], s_ks[4 * wave + 3]));
+      w_hi = min(min(s_ke[4 * wave], s_ke[4 * wave + 1]), min(s_ke[4 * wave + 2], s_ke[4 * wave + 3]));
+    }
+    w_hi = min(w_hi, tile_end);
+    // This lane's two 16-byte B chunks inside a tile: key f * 16 + l % 16, swizzled by key & 7,
+    // which is l & 7 for every fragment f.
+    const int kl = lane & 15;
+    const int boff0 = kl * kDim + (((2 * (lane >> 4)) ^ (kl & 7)) * 16);
+    const int boff1 = kl * kDim + (((2 * (lane >> 4) + 1) ^ (kl & 7)) * 16);
 
     v4i stage[kChunksPerThread];
     float stage_scale = 0.f;
@@ -166,22 +180,32 @@ __global__ __launch_bounds__(64 * WAVES, 2) void logits_ragged_kernel(RaggedLogi
       lstore(buf);
       __syncthreads();
       if (it + 1 < ntiles) gload(tile + kTileKeys);
+      const uint8_t* tbase = &s_kv[buf][0];
+      if (tile >= w_lo && tile + kTileKeys <= w_hi) {
+        // interior tile: every key is inside every row's window
+        float* __restrict__ optr = out_row + tile + kl;
 #pragma unroll
-      for (int f = 0; f < kTileKeys / 16; ++f) {
-        const int key = f * 16 + (lane & 15);
-        const uint8_t* base = &s_kv[buf][key * kDim];
-        const int c0 = (2 * (lane >> 4)) ^ (key & 7);
-        const int c1 = (2 * (lane >> 4) + 1) ^ (key & 7);
-        const v4i b0 = *reinterpret_cast<const v4i*>(base + c0 * 16);
-        const v4i b1 = *reinterpret_cast<const v4i*>(base + c1 * 16);
-        const v8i b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-        const float v = fragment_logit(qf, b) * s_scale[buf][key];
-        const int j = tile + key;
-        if (row_ok && j < tile_end) {
-          if (j >= my_ks && j < my_ke) {
-            out_row[j] = v;
-          } else if (clean) {
-            out_row[j] = -INFINITY;
+        for (int f = 0; f < kTileKeys / 16; ++f) {
+          const v4i b0 = *reinterpret_cast<const v4i*>(tbase + f * 16 * kDim + boff0);
+          const v4i b1 = *reinterpret_cast<const v4i*>(tbase + f * 16 * kDim + boff1);
+          const v8i b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+          optr[f * 16] = fragment_logit(qf, b) * s_scale[buf][f * 16 + kl];
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < kTileKeys / 16; ++f) {
+          const int key = f * 16 + kl;
+          const v4i b0 = *reinterpret_cast<const v4i*>(tbase + f * 16 * kDim + boff0);
+          const v4i b1 = *reinterpret_cast<const v4i*>(tbase + f * 16 * kDim + boff1);
+          const v8i b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+          const float v = fragment_logit(qf, b) * s_scale[buf][key];
+          const int j = tile + key;
+          if (row_ok && j < tile_end) {
+            if (j >= my_ks && j < my_ke) {
+              out_row[j] = v;
+            } else if (clean) {
+              out_row[j] = -INFINITY;
+            }
           }
         }
       }
