@@ -111,3 +111,32 @@ def test_topk_determinism():
     a = _run_topk(x, None, ke, 2048)
     b = _run_topk(x, None, ke, 2048)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "wide_range"])
+@pytest.mark.parametrize("rows,width,k", [(3, 40000, 3000), (50, 20000, 8192), (2, 70000, 16384),
+                                          (4, 16384, 16384)])
+def test_topk_large_k(kind, rows, width, k):
+    # k past ~2800 selects with the 16384-entry candidate list; k = 16384 is the largest supported
+    rng = np.random.default_rng(rows + width + k)
+    x = _logits(rng, rows, width, kind)
+    ks = np.zeros(rows, np.int32)
+    ke = np.full(rows, width, np.int32)
+    ke[0] = min(width, k - 5)                      # fewer keys than k
+    g = _run_topk(x, ks, ke, k)
+    assert_topk_exact(g, topk_indices(x, ks, ke, k), what=f"{kind} rows{rows} width{width} k{k}")
+
+
+@pytest.mark.parametrize("col0,ld", [(1, 1003), (3, 5003), (0, 5001)])
+def test_topk_unaligned_rows(col0, ld):
+    # rows that do not start on 16 bytes take the 4-byte load path
+    rng = np.random.default_rng(col0 + ld)
+    rows, width, k = 6, ld - col0 - 2, 200
+    base = _logits(rng, rows, ld, "normal")
+    x = torch.from_numpy(base).cuda()[:, col0:col0 + width]
+    ks = rng.integers(0, 50, rows).astype(np.int32)
+    ke = np.full(rows, width, np.int32)
+    g = F.indexer_topk(x, to_dev(ke), k, ks=to_dev(ks), width=width)
+    torch.cuda.synchronize()
+    e = topk_indices(base[:, col0:col0 + width], ks, ke, k)
+    assert_topk_exact(g.cpu().numpy(), e, what=f"col0 {col0} ld {ld}")
