@@ -39,7 +39,10 @@ fp8idx_status current_device(DeviceInfo* out) {
     if (hipGetDeviceProperties(&p, dev) == hipSuccess) {
       g_dev_ok[dev] = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
       g_dev_info[dev].cu_count = p.multiProcessorCount;
-      if (g_dev_ok[dev]) fp8idx::query_ragged_occupancy(g_dev_info[dev]);
+      if (g_dev_ok[dev]) {
+        fp8idx::query_ragged_occupancy(g_dev_info[dev]);
+        fp8idx::query_paged_occupancy(g_dev_info[dev]);
+      }
     } else {
       g_dev_ok[dev] = 0;
     }

@@ -86,10 +86,12 @@ struct TopkPlan {
 struct DeviceInfo {
   int cu_count;
   int ragged_wgs_per_cu;   // resident workgroups of the ragged logits kernel per CU
+  int paged_wgs_per_cu;    // resident workgroups of the paged logits kernel per CU
 };
 
 // Fills the occupancy fields of `d` (called once per device).
 void query_ragged_occupancy(DeviceInfo& d);
+void query_paged_occupancy(DeviceInfo& d);
 
 TopkPlan plan_topk(int32_t rows, int64_t width, int32_t k);
 size_t topk_workspace_bytes(const TopkPlan& p);

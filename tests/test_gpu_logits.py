@@ -164,6 +164,77 @@ def test_paged_invalid_page_ids_are_masked():
         assert np.all(d <= 1e-3 + 2e-3 * np.abs(o[r, keep]))
 
 
+@pytest.mark.parametrize("B,next_n", [(150, 1), (70, 3), (40, 6)])
+def test_paged_many_units_and_empty_rows(B, next_n):
+    """More (request, 4-row group) units than one wave-wide scan covers, with empty and one-key
+    contexts mixed in, so the persistent grid's page ranges start and end inside units and skip
+    units that own no pages."""
+    rng = np.random.default_rng(B * 7 + next_n)
+    ctx = rng.integers(0, 700, B)
+    ctx[rng.random(B) < 0.2] = 0
+    ctx[::17] = 1
+    ctx[0] = 700
+    inp = paged_inputs(B, next_n, 0, 700, 16, seed=40 + B, page_size=64, ctx=ctx)
+    width = inp.max_pages * 64
+    g = _run_paged(inp, width)
+    o = paged_mqa_logits(inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len,
+                         inp.block_table, inp.page_size, width=width)
+    assert_logits_close(g, o, np.zeros(inp.rows, np.int64), inp.row_len, clean=True,
+                        what=f"paged many units B{B} next_n{next_n}")
+
+
+def test_paged_clean_false_writes_only_inside_width():
+    """clean=0: [0, row_len) matches the oracle, [row_len, width) holds -inf or the old value,
+    and nothing at or past the width is touched."""
+    inp = paged_inputs(6, 4, 100, 1500, 16, seed=41, page_size=64)
+    width = inp.max_pages * 64
+    ld = width + 36
+    args = [to_dev(a) for a in (inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len, inp.block_table)]
+    out = torch.full((inp.rows, ld), 12345.0, dtype=torch.float32, device="cuda")
+    F.indexer_logits_paged(*args, width=width, clean=False, logits=out)
+    torch.cuda.synchronize()
+    g = out.cpu().numpy()
+    o = paged_mqa_logits(inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len,
+                         inp.block_table, inp.page_size, width=width)
+    for r in range(inp.rows):
+        n = int(inp.row_len[r])
+        d = np.abs(g[r, :n] - o[r, :n])
+        assert np.all(d <= 1e-3 + 2e-3 * np.abs(o[r, :n])), r
+        tail = g[r, n:width]
+        assert np.all((tail == 12345.0) | (tail == -np.inf)), r
+        assert np.all(g[r, width:] == 12345.0), r
+
+
+def test_paged_long_contexts_many_pages_per_wave():
+    """Contexts of 120K-131K keys for 96 requests: every wave of the persistent grid takes far
+    more than 64 pages, so page ids are read in several segments.  Pages are drawn with
+    repetition from a small pool (the kernel does not need distinct pages); sampled rows are
+    checked against the oracle over the full width."""
+    import dataclasses
+    B, nn = 96, 2
+    base = paged_inputs(B, nn, 4096, 4096, 16, seed=42, page_size=64)
+    rng = np.random.default_rng(42)
+    ctx = rng.integers(120000, 131073, B)
+    max_pages = 2048
+    P = base.kv_pool.shape[0]
+    bt = rng.integers(0, P, (B, max_pages)).astype(np.int32)
+    pages = (ctx + 63) // 64
+    for b in range(B):
+        bt[b, pages[b]:] = -1
+    row_len = np.array([ctx[b] - nn + r + 1 for b in range(B) for r in range(nn)], np.int32)
+    inp = dataclasses.replace(base, ctx=ctx.astype(np.int32), row_len=row_len, block_table=bt)
+    width = max_pages * 64
+    args = [to_dev(a) for a in (inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len, inp.block_table)]
+    g = F.indexer_logits_paged(*args, width=width, clean=True)
+    torch.cuda.synchronize()
+    rows = [0, 1, 77, 150, 190, 191]
+    L = paged_mqa_logits(inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len,
+                         inp.block_table, inp.page_size, width=width, rows=rows)
+    gs = g.cpu().numpy()[np.array(rows)]
+    assert_logits_close(gs, L, np.zeros(len(rows), np.int64), row_len[np.array(rows)], clean=True,
+                        what="paged long contexts")
+
+
 def test_paged_equals_ragged_on_gathered_kv():
     inp = paged_inputs(2, 4, 900, 1500, 16, seed=33, page_size=64)
     width = int(inp.row_len.max())
