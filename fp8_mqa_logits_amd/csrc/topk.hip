@@ -148,7 +148,8 @@ __device__ __forceinline__ int map_request(const TopkMap m, int grow) {
 // LDS of one workgroup.
 template <int NW, int CAP>
 struct TopkShared {
-  v2u cand[CAP];                    // candidates (code, position); bitmaps in the fallback
+  v2u cand[CAP + 1];                // candidates (code, position); bitmaps in the fallback;
+                                    // [CAP] absorbs appends past the end (the count still grows)
   uint32_t hist[kBitmapWords];      // digit histogram, later per-word prefix popcounts
   uint32_t bits[kBitmapWords];      // position bitmap
   uint32_t bk[kBoundaryMax];        // codes of the candidates in the boundary bin
@@ -167,7 +168,7 @@ struct TopkShared {
 // <= total), with the number of elements in higher bins (above) and in the
 // bin itself (count).  Ends with a barrier.
 template <int THREADS, int CAP>
-__device__ void pick_bin(uint32_t need, uint32_t& bin, uint32_t& above, uint32_t& count,
+__device__ __forceinline__ void pick_bin(uint32_t need, uint32_t& bin, uint32_t& above, uint32_t& count,
                          TopkShared<THREADS / 64, CAP>& sh) {
   constexpr int NW = THREADS / 64;
   constexpr int DPT = kBins / THREADS;
@@ -220,7 +221,7 @@ __device__ void pick_bin(uint32_t need, uint32_t& bin, uint32_t& above, uint32_t
 // has at most slack elements and return that bin's lowest code: then between
 // rank and rank + slack - 1 elements are >= the result (`need` is not set).
 template <int THREADS, int CAP, typename ForEach>
-__device__ uint32_t radix_select(ForEach for_each, uint32_t lo, uint32_t hi, uint32_t rank, uint32_t slack,
+__device__ __forceinline__ uint32_t radix_select(ForEach for_each, uint32_t lo, uint32_t hi, uint32_t rank, uint32_t slack,
                                  uint32_t& need, TopkShared<THREADS / 64, CAP>& sh) {
   constexpr int DPT = kBins / THREADS;
   const int tid = threadIdx.x;
@@ -364,14 +365,75 @@ struct SegmentSource {
       }
     }
   }
+  // raw keys of positions [v * VEC, v * VEC + VEC): level 0 float bits, other levels codes
+  __device__ __forceinline__ void load_raw(int v, uint32_t* c) const {
+    if (LEVEL0) {
+      if (VEC == 4) {
+        const v4i t = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(f) + v);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) c[i] = (uint32_t)t[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) c[i] = __float_as_uint(__builtin_nontemporal_load(f + v * VEC + i));
+      }
+    } else {
+      load(v, c);
+    }
+  }
+  __device__ __forceinline__ static uint32_t raw_code(uint32_t r) { return LEVEL0 ? float_code(__uint_as_float(r)) : r; }
   __device__ __forceinline__ uint32_t code_at(int pos) const { return LEVEL0 ? float_code(f[pos]) : u[pos]; }
   __device__ __forceinline__ bool valid(int pos) const { return pos >= off && pos < span; }
 };
+
+// Appends this lane's candidates among one streaming pass's keys c (raw keys,
+// vector v of slot u at v0 + u * THREADS) to the LDS list, at slots claimed
+// wave-wide with one LDS atomic.  FAST: every vector lies in the window and a
+// key is a candidate when its bits, read as a signed int, reach Ti (level 0
+// with the threshold above +0.0); otherwise the general test on codes.
+template <bool FAST, int THREADS, int CAP, int UNR, int VEC, bool LEVEL0, typename Shared>
+__device__ __forceinline__ void append_candidates(const uint32_t (&c)[UNR][VEC], int v0, int nvec,
+                                                  const SegmentSource<LEVEL0, VEC>& src, uint32_t T, int Ti,
+                                                  int lane, Shared& sh) {
+  auto is_cand = [&](int u, int i) -> bool {
+    if (FAST) return (int)c[u][i] >= Ti;
+    const int v = v0 + u * THREADS;
+    return v < nvec && src.valid(v * VEC + i) && SegmentSource<LEVEL0, VEC>::raw_code(c[u][i]) >= T;
+  };
+  auto code_of = [](uint32_t r) -> uint32_t {
+    return FAST ? (r | 0x80000000u) : SegmentSource<LEVEL0, VEC>::raw_code(r);
+  };
+  uint32_t mine = 0u;
+#pragma unroll
+  for (int u = 0; u < UNR; ++u)
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) mine += is_cand(u, i) ? 1u : 0u;
+  uint32_t incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = (uint32_t)__shfl_up((int)incl, o);
+    if (lane >= o) incl += t;
+  }
+  const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+  if (total == 0u) return;
+  uint32_t base = 0u;
+  if (lane == 63) base = atomicAdd(&sh.cnt, total);
+  base = __builtin_amdgcn_readlane(base, 63);
+  uint32_t slot = base + incl - mine;
+#pragma unroll
+  for (int u = 0; u < UNR; ++u)
+#pragma unroll
+    for (int i = 0; i < VEC; ++i)
+      if (is_cand(u, i)) {
+        sh.cand[min(slot, (uint32_t)CAP)] = v2u{code_of(c[u][i]), (uint32_t)((v0 + u * THREADS) * VEC + i)};
+        ++slot;
+      }
+}
 
 template <int THREADS, int CAP, bool LEVEL0, bool FINAL, int VEC>
 __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
   constexpr int NW = THREADS / 64;
   constexpr int UNR = kElemsPerPass / VEC;   // vectors per thread per pass
+  static_assert(kElemsPerPass <= 32, "a pass's candidate flags are one 32-bit mask per thread");
   static_assert(kBins % THREADS == 0, "bins per thread");
   static_assert(CAP >= kBitmapWords, "fallback bitmaps reuse the candidate list");
   static_assert(THREADS == kTopkThreads, "sample runs are one workgroup wide");
@@ -503,12 +565,20 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
   uint32_t C = 0xffffffffu;
   if (try_list) {
     // Every lane runs every pass (the slot scan below is wave-wide); the next
-    // pass's loads are in flight while this pass's keys are appended.
+    // pass's loads are in flight while this pass's keys are appended.  Keys are
+    // loaded raw.  With the threshold above +0.0, a level-0 key is a candidate
+    // exactly when its bits, read as a signed int, reach T - 2^31: negative
+    // floats, -0.0 and negative NaNs are negative ints, and the code of a
+    // non-negative float is its bits with the sign bit set.  A pass whose
+    // vectors all lie in the window then costs one compare per key; other
+    // passes take the general test on codes.
     constexpr int kPass = THREADS * UNR;
     auto load_pass = [&](int vb, uint32_t (&dst)[UNR][VEC]) {
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) src.load(min(vb + tid + u * THREADS, nvec - 1), dst[u]);
+      for (int u = 0; u < UNR; ++u) src.load_raw(min(vb + tid + u * THREADS, nvec - 1), dst[u]);
     };
+    const bool raw_cmp = LEVEL0 && T > 0x80000000u;
+    const int Ti = (int)(T - 0x80000000u);
     uint32_t c[UNR][VEC];
     if (nvec > 0) load_pass(0, c);
     for (int vb = 0; vb < nvec; vb += kPass) {
@@ -516,41 +586,10 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
       const bool more = vb + kPass < nvec;
       if (more) load_pass(vb + kPass, nx);
       const int v0 = vb + tid;
-      uint32_t mask = 0u;
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int v = v0 + u * THREADS;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-          const int pos = v * VEC + i;
-          const bool cand = v < nvec && src.valid(pos) && c[u][i] >= T;
-          mask |= (uint32_t)cand << (u * VEC + i);
-        }
-      }
-      // claim slots for the wave's candidates: exclusive scan of the counts
-      const uint32_t mine = (uint32_t)__popc(mask);
-      uint32_t incl = mine;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = (uint32_t)__shfl_up((int)incl, o);
-        if (lane >= o) incl += t;
-      }
-      const uint32_t total = (uint32_t)__shfl((int)incl, 63);
-      if (total != 0u) {
-        uint32_t base = 0u;
-        if (lane == 63) base = atomicAdd(&sh.cnt, total);
-        uint32_t slot = (uint32_t)__shfl((int)base, 63) + incl - mine;
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) {
-            if (mask & (1u << (u * VEC + i))) {
-              if (slot < (uint32_t)CAP) sh.cand[slot] = v2u{c[u][i], (uint32_t)((v0 + u * THREADS) * VEC + i)};
-              ++slot;
-            }
-          }
-        }
-      }
+      if (raw_cmp && vb * VEC >= src.off && (vb + kPass) * VEC <= src.span)
+        append_candidates<true, THREADS, CAP, UNR, VEC>(c, v0, nvec, src, T, Ti, lane, sh);
+      else
+        append_candidates<false, THREADS, CAP, UNR, VEC>(c, v0, nvec, src, T, Ti, lane, sh);
       if (more) {
 #pragma unroll
         for (int u = 0; u < UNR; ++u)
