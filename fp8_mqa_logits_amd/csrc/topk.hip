@@ -512,6 +512,16 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
     sh.nb = 0u;
   }
 
+  // Streaming passes of the compaction below: pass 0 is loaded as soon as the
+  // sample's loads are issued, so it arrives while the threshold is chosen.
+  constexpr int kPass = THREADS * UNR;
+  auto load_pass = [&](int vb, uint32_t (&dst)[UNR][VEC]) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) src.load_raw(min(vb + tid + u * THREADS, nvec - 1), dst[u]);
+  };
+  uint32_t c[UNR][VEC];
+  bool c_loaded = false;
+
   // ---- 1. candidate threshold ------------------------------------------------
   uint32_t T = 1u;          // lowest candidate code; 1 takes every key
   bool sampled = false;     // T came from the sample
@@ -524,6 +534,11 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
     for (int b = 0; b < kSampleRuns; ++b) {
       const int start = src.off + (int)((int64_t)b * (len - THREADS) / (kSampleRuns - 1));
       sc[b] = src.code_at(start + tid);
+    }
+    if (nvec > 0) {
+      load_pass(0, c);
+      c_loaded = true;
+      __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of the threshold work
     }
     uint32_t smin = 0xffffffffu, smax = 0u, ns = 0u;
 #pragma unroll
@@ -572,15 +587,9 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
     // non-negative float is its bits with the sign bit set.  A pass whose
     // vectors all lie in the window then costs one compare per key; other
     // passes take the general test on codes.
-    constexpr int kPass = THREADS * UNR;
-    auto load_pass = [&](int vb, uint32_t (&dst)[UNR][VEC]) {
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) src.load_raw(min(vb + tid + u * THREADS, nvec - 1), dst[u]);
-    };
     const bool raw_cmp = LEVEL0 && T > 0x80000000u;
     const int Ti = (int)(T - 0x80000000u);
-    uint32_t c[UNR][VEC];
-    if (nvec > 0) load_pass(0, c);
+    if (nvec > 0 && !c_loaded) load_pass(0, c);
     for (int vb = 0; vb < nvec; vb += kPass) {
       uint32_t nx[UNR][VEC];
       const bool more = vb + kPass < nvec;
@@ -701,18 +710,23 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
     }
     if (!done) {
       // ---- exact selection on the whole list (dense ties, or an unsampled list) ----
-      uint32_t cmin = 0xffffffffu, cmax = 0u, unused = 0u;
-      for (uint32_t i = tid; i < C; i += THREADS) {
-        cmin = min(cmin, sh.cand[i].x);
-        cmax = max(cmax, sh.cand[i].x);
+      // A list of at most kk entries is taken whole: tau = 0 lies below every
+      // listed code (codes are >= 1), so no entry ties with it.
+      uint32_t need = 0u;
+      uint32_t tau = 0u;
+      if (C > kk) {
+        uint32_t cmin = 0xffffffffu, cmax = 0u, unused = 0u;
+        for (uint32_t i = tid; i < C; i += THREADS) {
+          cmin = min(cmin, sh.cand[i].x);
+          cmax = max(cmax, sh.cand[i].x);
+        }
+        block_min_max_sum<NW>(cmin, cmax, unused, sh.w0, sh.w1, sh.w2);
+        tau = radix_select<THREADS, CAP>(
+            [&](auto&& visit) {
+              for (uint32_t i = tid; i < C; i += THREADS) visit(sh.cand[i].x);
+            },
+            cmin, cmax, kk, 0u, need, sh);
       }
-      block_min_max_sum<NW>(cmin, cmax, unused, sh.w0, sh.w1, sh.w2);
-      uint32_t need;
-      const uint32_t tau = radix_select<THREADS, CAP>(
-          [&](auto&& visit) {
-            for (uint32_t i = tid; i < C; i += THREADS) visit(sh.cand[i].x);
-          },
-          cmin, cmax, kk, 0u, need, sh);
       uint32_t eq = 0u;
       for (uint32_t i = tid; i < C; i += THREADS) eq += sh.cand[i].x == tau;
       const uint32_t E = block_sum<NW>(eq, sh.w0);
