@@ -22,3 +22,9 @@ from .indexer_oracle import (  # noqa: F401
     rows_per_chunk,
     encode_e4m3fn,
 )
+from .sparse_mla_oracle import (  # noqa: F401
+    MLA_DQK,
+    MLA_DV,
+    decode_bf16,
+    sparse_mla,
+)
