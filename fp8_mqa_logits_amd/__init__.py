@@ -25,6 +25,10 @@ from .binding import (  # noqa: F401
     indexer_quant_fp8,
     indexer_prepare_ragged,
     indexer_prepare_decode,
+    indexer_sparse_mla,
+    fp8idx_sparse_mla_workspace_bytes,
+    MLA_DQK,
+    MLA_DV,
     fp8idx_workspace_bytes,
     fp8idx_workspace_bytes_paged,
     fp8idx_rows_per_chunk,

@@ -35,7 +35,11 @@ EXPORTED = (
     "fp8idx_status_string", "fp8idx_last_hip_error", "fp8idx_version",
     "indexer_quant_fp8", "indexer_logits_topk_ragged_overlap",
     "indexer_prepare_ragged", "indexer_prepare_decode",
+    "indexer_sparse_mla", "fp8idx_sparse_mla_workspace_bytes",
 )
+
+MLA_DQK = 576   # sparse MLA KV row: 512 latent + 64 rotary values
+MLA_DV = 512
 
 
 class Fp8idxError(RuntimeError):
@@ -95,6 +99,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "indexer_prepare_decode": (_I32, [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _I32, _P]),
         "indexer_logits_topk_ragged_overlap": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                                       ctypes.POINTER(_CMap), _P, _I64, _SZ, _P, _SZ, _P, _P]),
+        "indexer_sparse_mla": (_I32, [_P, _P, _P, _I64, _P, _I64, _I32, _I32, _I32, _I32, _I32, ctypes.c_float,
+                                      _P, _P, _P, _SZ, _P]),
+        "fp8idx_sparse_mla_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -462,3 +469,56 @@ def indexer_prepare_decode(seq_len, req_idx, req_to_page, next_n: int, *, max_pa
                                       _stream(dev, stream))
     _check("indexer_prepare_decode", st)
     return row_len, bt
+
+
+def fp8idx_sparse_mla_workspace_bytes(T: int, H: int, topk: int) -> int:
+    return int(load_library().fp8idx_sparse_mla_workspace_bytes(int(T), int(H), int(topk)))
+
+
+def indexer_sparse_mla(q, kv, kv_scale, indices, sm_scale: float, *, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                       workspace: Optional[torch.Tensor] = None, stream=None):
+    """Sparse MLA attention over top-k slots -> (out float32 [T, H, 512], lse float32 [T, H] or None).
+
+    q: bf16 [T, H, 576] (or int16 / uint16 bit patterns); kv: e4m3fn [S, 576] (or uint8 codes);
+    kv_scale: float32 [S]; indices: int32 [T, topk] slot ids (-1 or >= S skipped).
+    """
+    dev = _dev(q, "q")
+    q16 = _need(q, "q", (torch.bfloat16, torch.int16, torch.uint16), dev)
+    kv8 = _fp8(kv, "kv", dev)
+    _need(kv_scale, "kv_scale", _F32, dev)
+    _need(indices, "indices", _I32T, dev)
+    if q16.dim() != 3 or q16.shape[2] != MLA_DQK:
+        raise ValueError("q must be [T, H, 576]")
+    if kv8.dim() != 2 or kv8.shape[1] != MLA_DQK or kv_scale.numel() != kv8.shape[0]:
+        raise ValueError("kv must be [S, 576] with kv_scale [S]")
+    T, Hh = q16.shape[0], q16.shape[1]
+    if indices.dim() != 2 or indices.shape[0] != T:
+        raise ValueError("indices must be [T, topk]")
+    topk = indices.shape[1]
+    if out is None:
+        out = torch.empty((T, Hh, MLA_DV), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", _F32, dev)
+    if lse is None and want_lse:
+        lse = torch.empty((T, Hh), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _need(lse, "lse", _F32, dev)
+    L = load_library()
+    need = int(L.fp8idx_sparse_mla_workspace_bytes(T, Hh, topk)) if T > 0 else 0
+    ws = None
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace too small: {workspace.numel()} < {need}")
+        base = workspace.data_ptr()
+        ws = (base + 255) // 256 * 256
+        if ws + need > base + workspace.numel():
+            raise ValueError("workspace too small after 256-byte alignment")
+    with torch.cuda.device(dev):
+        st = L.indexer_sparse_mla(_ptr(q16), _ptr(kv8), _ptr(kv_scale), kv8.shape[0], _ptr(indices), topk, T, Hh,
+                                  MLA_DQK, MLA_DV, topk, float(sm_scale), _ptr(out), _ptr(lse), ws, need,
+                                  _stream(dev, stream))
+    _check("indexer_sparse_mla", st)
+    return out, lse

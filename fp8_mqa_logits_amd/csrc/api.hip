@@ -198,6 +198,33 @@ int32_t fp8idx_rows_per_chunk(size_t logits_cap_bytes, int64_t width, int32_t ro
   return rows_per_chunk(logits_cap_bytes, ws_logits_ld(width), rows);
 }
 
+size_t fp8idx_sparse_mla_workspace_bytes(int32_t T, int32_t H, int32_t topk) {
+  if (T <= 0 || H <= 0 || topk < 1) return 0;
+  return fp8idx::plan_sparse_mla(T, H, topk).ws_bytes;
+}
+
+fp8idx_status indexer_sparse_mla(const uint16_t* q, const uint8_t* kv, const float* kv_scale, int64_t num_slots,
+                                 const int32_t* indices, int64_t ld_indices, int32_t T, int32_t H, int32_t D,
+                                 int32_t Dv, int32_t topk, float sm_scale, float* out, float* lse, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (D != fp8idx::kMlaDqk || Dv != fp8idx::kMlaDv || H <= 0 || H % 16 != 0) return FP8IDX_EUNSUPPORTED;
+  if (T < 0 || topk < 1 || ld_indices < topk || num_slots < 1) return FP8IDX_EINVAL;
+  if ((int64_t)T * H > INT32_MAX) return FP8IDX_EINVAL;
+  if (T == 0) return FP8IDX_OK;
+  if (!q || !kv || !kv_scale || !indices || !out) return FP8IDX_EINVAL;
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16) || !aligned(kv_scale, 4) || !aligned(indices, 4) ||
+      (lse && !aligned(lse, 4)))
+    return FP8IDX_EINVAL;
+  const fp8idx::SparseMlaPlan plan = fp8idx::plan_sparse_mla(T, H, topk);
+  if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes)) return FP8IDX_EWORKSPACE;
+  if (plan.ws_bytes > 0 && !aligned(ws, 256)) return FP8IDX_EINVAL;
+  DeviceInfo dev;
+  if (fp8idx_status s = current_device(&dev)) return s;
+  fp8idx::SparseMlaArgs a{q, kv, kv_scale, num_slots, indices, ld_indices, T, H, topk, sm_scale, out, lse};
+  const hipError_t e = fp8idx::launch_sparse_mla(a, plan, ws, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8IDX_OK : hip_fail(e);
+}
+
 size_t fp8idx_workspace_bytes(int32_t op, int32_t rows, int64_t width, int32_t k, size_t logits_cap_bytes) {
   if (rows <= 0 || width < 0 || k < 1 || k > fp8idx::kMaxK) return 0;
   switch (op) {

@@ -143,4 +143,30 @@ struct QuantArgs {
 hipError_t launch_quant_fp8(const QuantArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, const TopkPlan& plan, void* ws, hipStream_t s);
 
+// Sparse MLA attention over top-k slots (sparse_mla.hip).
+constexpr int kMlaDqk = 576;   // KV row: 512 latent + 64 rotary values
+constexpr int kMlaDv = 512;    // value: the latent part
+constexpr int kMlaBlock = 64;  // keys staged per step
+struct SparseMlaArgs {
+  const uint16_t* q;        // bf16 [T, H, 576]
+  const uint8_t* kv;        // e4m3fn [S, 576]
+  const float* kv_scale;    // [S]
+  int64_t num_slots;
+  const int32_t* indices;   // [T, ld_idx]
+  int64_t ld_idx;
+  int32_t T;
+  int32_t H;
+  int32_t topk;
+  float sm_scale;
+  float* out;               // [T, H, 512]
+  float* lse;               // [T, H] or null
+};
+struct SparseMlaPlan {
+  int32_t nsplit;           // key ranges per (token, head block)
+  int32_t keys_per_split;   // a multiple of kMlaBlock
+  size_t ws_bytes;          // partial outputs when nsplit > 1
+};
+SparseMlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t topk);
+hipError_t launch_sparse_mla(const SparseMlaArgs& a, const SparseMlaPlan& plan, void* ws, hipStream_t s);
+
 }  // namespace fp8idx

@@ -1,0 +1,367 @@
+// Sparse MLA attention over the indexer's top-k slots, for gfx950 (the sparse
+// MLA prefill / decode step that consumes the indexer on the vessl-ai/sglang
+// PR #87 page, which keeps the MLA KV pool in fp8 e4m3 and widens it to bf16
+// inside the kernel, and runs few-token decode as split-K partials plus a
+// combine).
+//
+//   s[t, h, i] = sm_scale * dot(q[t, h, :], kv_scale[j] * e4m3(kv[j, :]))      j = idx[t, i], 0 <= j < S
+//   o[t, h, :] = softmax_i(s[t, h, :]) @ (kv_scale[j] * e4m3(kv[j, :512]))
+//   lse[t, h]  = log sum_i exp(s[t, h, i])
+//
+// Work decomposition
+// - A workgroup takes one token, one range of its top-k list (a split) and one
+//   block of 64 heads.  Each of its 4 waves owns 16 heads: their q stays in
+//   VGPRs as bf16 MFMA operands and their output (16 heads x 512 values, in
+//   accumulation registers) with its online-softmax state.  One wave per SIMD
+//   leaves each wave the whole register file.  The splits merge in a second
+//   kernel.
+// - Keys stream through LDS in 64-key steps, double buffered, as fp8: once
+//   row-major (576 bytes per key, for the scores) and once transposed (keys
+//   contiguous per latent dimension, for the value product).  Each thread
+//   gathers two 16-byte latent chunks of 4 keys and one rotary chunk, and
+//   transposes its 4 x 4 byte tiles with byte permutes while storing, so no
+//   extra LDS pass is needed.  The gather for step i + 2 is in flight while
+//   step i is computed.
+// - Scores are computed transposed, S^T = K Q^T (16x16x32 bf16 MFMA, fp8
+//   widened to bf16 exactly at operand load): a lane then holds 4 consecutive
+//   keys of one head, which is exactly the A-operand layout of P in P V, so
+//   the probabilities never leave registers.  The value operand reads 4 + 4
+//   transposed fp8 bytes per lane.
+// - Softmax works in log2 units; the running maximum is raised (and the
+//   output rescaled) only when a step's maximum exceeds it by more than 8,
+//   which keeps every weight below 2^8 and skips most rescales.
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+#include <algorithm>
+
+namespace fp8idx {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+constexpr int kMlaThreads = 256;
+constexpr int kMlaHeadsPerWg = 64;
+constexpr int kKRow = kMlaDqk + 8;            // LDS bytes per key, row-major (8 bytes of bank skew)
+constexpr int kVtRow = kMlaBlock + 4;         // LDS bytes per latent dimension, transposed
+constexpr int kKBytes = kMlaBlock * kKRow;    // 37376
+constexpr int kVtBytes = kMlaDv * kVtRow;     // 34816
+constexpr int kKSteps = kMlaDqk / 32;         // 18 score k-steps of 32 values
+constexpr int kVTiles = kMlaDv / 16;          // 32 output tiles of 16 values
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;                 // log2 slack before the running maximum moves
+
+struct MlaStage {
+  uint8_t k[2][kKBytes];
+  uint8_t vt[2][kVtBytes];
+  float mul[2][kMlaBlock];   // sm_scale * log2(e) * kv_scale; NaN marks a masked key
+  float vsc[2][kMlaBlock];   // kv_scale; 0 for a masked key
+};
+// 8 e4m3fn bytes (w0 bytes 0..3, then w1 bytes 0..3) -> 8 bf16, exactly.
+__device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 4 x 4 byte transpose: y[i] byte q = x[q] byte i.
+__device__ __forceinline__ void transpose4x4(const uint32_t (&x)[4], uint32_t (&y)[4]) {
+  const uint32_t t0 = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);
+  const uint32_t t1 = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);
+  const uint32_t t2 = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
+  y[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  y[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  y[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  y[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+__global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArgs a, int nsplit,
+                                                                    int keys_per_split, float* part_o,
+                                                                    float* part_lse) {
+  __shared__ __attribute__((aligned(16))) MlaStage sh;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ht = wave;   // head tile of the block
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+  const int t = blockIdx.x / nsplit;
+  const int sp = blockIdx.x - t * nsplit;
+  const int hb = blockIdx.y;
+  const int k_begin = sp * keys_per_split;
+  const int k_end = min(a.topk, k_begin + keys_per_split);
+  const int nblk = k_end > k_begin ? (k_end - k_begin + kMlaBlock - 1) / kMlaBlock : 0;
+  const int32_t* __restrict__ idx_row = a.indices + (int64_t)t * a.ld_idx;
+
+  // ---- q of this wave's head tile: B operand of S^T (lane: head l16, values 32 ks + 8 g .. +8)
+  const int head0 = hb * kMlaHeadsPerWg + ht * 16;   // first head of the tile (H is a multiple of 16)
+  const bool head_ok = head0 < a.H;
+  v8bf qf[kKSteps];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)t * a.H + (head_ok ? head0 + l16 : 0)) * kMlaDqk;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      v4i raw = {0, 0, 0, 0};
+      if (head_ok) raw = *reinterpret_cast<const v4i*>(qrow + 32 * ks + 8 * g);
+      qf[ks] = __builtin_bit_cast(v8bf, raw);
+    }
+  }
+
+  // ---- staging: this thread's two latent chunks of a key quad, one rotary chunk, one scale
+  const int sq = tid >> 4;            // keys 4 sq .. 4 sq + 3 of the step
+  const int sc = tid & 15;            // latent chunks sc and sc + 16 (16 values each)
+  const int rk = tid >> 2;            // rotary: key rk, chunk 32 + (tid & 3)
+  const int rc = 32 + (tid & 3);
+  v4i st_lat[4][2];
+  v4i st_rot;
+  float st_scale = 0.f;
+  bool st_ok = false;
+  // Every load is unconditional: a masked key (past the range, or an invalid
+  // slot) reads slot 0 and is masked by its scale entry.
+  auto slot_of = [&](int blk, int key, bool& ok) -> int64_t {
+    const int kk = k_begin + blk * kMlaBlock + key;
+    const int32_t j = kk < k_end ? idx_row[kk] : -1;
+    ok = j >= 0 && (int64_t)j < a.num_slots;
+    return ok ? (int64_t)j : 0;
+  };
+  auto stage_load = [&](int blk) {
+    bool ok;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const uint8_t* row = a.kv + slot_of(blk, 4 * sq + q4, ok) * kMlaDqk;
+      st_lat[q4][0] = *reinterpret_cast<const v4i*>(row + 16 * sc);
+      st_lat[q4][1] = *reinterpret_cast<const v4i*>(row + 16 * (sc + 16));
+    }
+    st_rot = *reinterpret_cast<const v4i*>(a.kv + slot_of(blk, rk, ok) * kMlaDqk + 16 * rc);
+    if (tid < kMlaBlock) {
+      const int64_t j = slot_of(blk, tid, st_ok);
+      st_scale = a.kv_scale[j];
+    }
+  };
+  auto stage_store = [&](int buf) {
+    uint8_t* K = sh.k[buf];
+    uint8_t* Vt = sh.vt[buf];
+    // rows are 8-byte aligned (584-byte stride), so 16-byte chunks go out as two 8-byte stores
+    auto put16 = [](uint8_t* dst, const v4i& v) {
+      reinterpret_cast<uint2*>(dst)[0] = uint2{(uint32_t)v[0], (uint32_t)v[1]};
+      reinterpret_cast<uint2*>(dst)[1] = uint2{(uint32_t)v[2], (uint32_t)v[3]};
+    };
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      put16(K + (4 * sq + q4) * kKRow + 16 * sc, st_lat[q4][0]);
+      put16(K + (4 * sq + q4) * kKRow + 16 * (sc + 16), st_lat[q4][1]);
+    }
+    put16(K + rk * kKRow + 16 * rc, st_rot);
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      const int chunk = sc + 16 * ch;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x[4] = {(uint32_t)st_lat[0][ch][w], (uint32_t)st_lat[1][ch][w], (uint32_t)st_lat[2][ch][w],
+                               (uint32_t)st_lat[3][ch][w]};
+        uint32_t y[4];
+        transpose4x4(x, y);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<uint32_t*>(Vt + (16 * chunk + 4 * w + i) * kVtRow + 4 * sq) = y[i];
+      }
+    }
+    if (tid < kMlaBlock) {
+      sh.mul[buf][tid] = st_ok ? a.sm_scale * kLog2e * st_scale : __builtin_nanf("");
+      sh.vsc[buf][tid] = st_ok ? st_scale : 0.f;
+    }
+  };
+
+  // ---- online softmax state (head l16; equal in the 4 lane groups) and output
+  float mrun = -INFINITY;
+  float lrun = 0.f;   // this lane's share of the denominator
+  v4f O[kVTiles];
+#pragma unroll
+  for (int n = 0; n < kVTiles; ++n) O[n] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  if (nblk > 0) {
+    stage_load(0);
+    stage_store(0);
+    if (nblk > 1) stage_load(1);
+  }
+  __syncthreads();
+
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int cb = blk & 1;
+    const uint8_t* K = sh.k[cb];
+    const uint8_t* Vt = sh.vt[cb];
+
+    // scores S^T: tile kt rows = keys 16 kt + 4 g + r, column = head l16
+    v4f S[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) S[kt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const uint8_t* p = K + (16 * kt + l16) * kKRow + 32 * ks + 8 * g;
+        const uint2 w = *reinterpret_cast<const uint2*>(p);
+        S[kt] = mfma_bf16(fp8x8_to_bf16(w.x, w.y), qf[ks], S[kt]);
+      }
+    }
+
+    // to log2 units, masked keys to -inf; the step's maximum per head
+    float bm = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const v4f mul = *reinterpret_cast<const v4f*>(&sh.mul[cb][16 * kt + 4 * g]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = mul[r] != mul[r] ? -INFINITY : S[kt][r] * mul[r];
+        S[kt][r] = x;
+        bm = fmaxf(bm, x);
+      }
+    }
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    // lazy rescale: move the running maximum only when this step exceeds it by more than kLazy
+    const bool need = bm > mrun + kLazy || (mrun == -INFINITY && bm > -INFINITY);
+    if (ballot64(need) != 0ull) {
+      const float mnew = need ? bm : mrun;
+      const float alpha = mnew == mrun ? 1.f : exp2f(mrun - mnew);
+      lrun *= alpha;
+      mrun = mnew;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 4 * g + r);
+#pragma unroll
+        for (int n = 0; n < kVTiles; ++n) O[n][r] *= ar;
+      }
+    }
+    // probabilities times kv_scale, as the A operands of P V: key step ks2 holds
+    // keys 32 ks2 + 4 g .. +4 (tile 2 ks2) and 32 ks2 + 16 + 4 g .. +4 (tile 2 ks2 + 1)
+    v8bf P[2];
+    {
+      float ps = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const v4f vsc = *reinterpret_cast<const v4f*>(&sh.vsc[cb][16 * kt + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pr = mrun == -INFINITY ? 0.f : exp2f(S[kt][r] - mrun);
+          ps += pr;
+          P[kt >> 1][4 * (kt & 1) + r] = (__bf16)(pr * vsc[r]);
+        }
+      }
+      lrun += ps;
+    }
+    // O += P V: value tile n, lane column 16 n + l16
+#pragma unroll
+    for (int n = 0; n < kVTiles; ++n) {
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const uint8_t* vp = Vt + (16 * n + l16) * kVtRow + 32 * ks2 + 4 * g;
+        const uint32_t w0 = *reinterpret_cast<const uint32_t*>(vp);
+        const uint32_t w1 = *reinterpret_cast<const uint32_t*>(vp + 16);
+        O[n] = mfma_bf16(P[ks2], fp8x8_to_bf16(w0, w1), O[n]);
+      }
+    }
+
+    // stage step blk + 1 into the other buffer (its loads were issued a step ago) and load step blk + 2
+    if (blk + 1 < nblk) stage_store(cb ^ 1);
+    if (blk + 2 < nblk) stage_load(blk + 2);
+    __syncthreads();
+  }
+
+  // ---- normalise and store
+  lrun += __shfl_xor(lrun, 16);
+  lrun += __shfl_xor(lrun, 32);
+  if (!head_ok) return;
+  const float inv = lrun > 0.f ? 1.f / lrun : 0.f;   // per head l16
+  if (g == 0) {
+    const float lse = lrun > 0.f ? (mrun + __log2f(lrun)) * kLn2 : -INFINITY;
+    const int head = head0 + l16;
+    if (nsplit == 1) {
+      if (a.lse) a.lse[(int64_t)t * a.H + head] = lse;
+    } else {
+      part_lse[((int64_t)t * nsplit + sp) * a.H + head] = lse;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float c = __shfl(inv, 4 * g + r);
+    const int head = head0 + 4 * g + r;
+    float* dst = nsplit == 1 ? a.out + ((int64_t)t * a.H + head) * kMlaDv
+                             : part_o + (((int64_t)t * nsplit + sp) * a.H + head) * kMlaDv;
+#pragma unroll
+    for (int n = 0; n < kVTiles; ++n) dst[16 * n + l16] = O[n][r] * c;
+  }
+}
+
+// Merges the splits of each (token, head): weights exp(lse_s - lse), lse = log sum exp(lse_s).
+__global__ __launch_bounds__(128) void sparse_mla_combine_kernel(SparseMlaArgs a, int nsplit, const float* part_o,
+                                                                 const float* part_lse) {
+  const int t = blockIdx.x;
+  const int head = blockIdx.y;
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_lse[((int64_t)t * nsplit + s) * a.H + head]);
+  float z = 0.f;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  if (m != -INFINITY) {
+    for (int s = 0; s < nsplit; ++s) {
+      const float ls = part_lse[((int64_t)t * nsplit + s) * a.H + head];
+      const float w = ls == -INFINITY ? 0.f : __expf(ls - m);
+      z += w;
+      const v4f v = *reinterpret_cast<const v4f*>(part_o + (((int64_t)t * nsplit + s) * a.H + head) * kMlaDv +
+                                                  4 * threadIdx.x);
+      acc += v * w;
+    }
+  }
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+  *reinterpret_cast<v4f*>(a.out + ((int64_t)t * a.H + head) * kMlaDv + 4 * threadIdx.x) = acc * inv;
+  if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)t * a.H + head] = z > 0.f ? m + __logf(z) : -INFINITY;
+}
+
+// Splits each top-k list so that about kMlaTargetWgs workgroups run (one per
+// CU of the 256-CU part), never below one 64-key step per split.  A pure
+// function of the shape, so the workspace size needs no device.
+constexpr int64_t kMlaTargetWgs = 256;
+
+SparseMlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t topk) {
+  SparseMlaPlan p{};
+  const int64_t blocks = std::max<int64_t>(1, ((int64_t)topk + kMlaBlock - 1) / kMlaBlock);
+  const int64_t groups = std::max<int64_t>(1, (int64_t)T * ((H + kMlaHeadsPerWg - 1) / kMlaHeadsPerWg));
+  int64_t nsplit = std::min<int64_t>(blocks, std::max<int64_t>(1, (kMlaTargetWgs + groups - 1) / groups));
+  const int64_t blocks_per_split = (blocks + nsplit - 1) / nsplit;
+  nsplit = (blocks + blocks_per_split - 1) / blocks_per_split;
+  p.nsplit = (int32_t)nsplit;
+  p.keys_per_split = (int32_t)(blocks_per_split * kMlaBlock);
+  p.ws_bytes = nsplit > 1 ? (size_t)T * (size_t)nsplit * (size_t)H * (kMlaDv + 1) * sizeof(float) + 256 : 0;
+  return p;
+}
+
+hipError_t launch_sparse_mla(const SparseMlaArgs& a, const SparseMlaPlan& plan, void* ws, hipStream_t s) {
+  if (a.T <= 0 || a.H <= 0) return hipSuccess;
+  float* part_o = nullptr;
+  float* part_lse = nullptr;
+  if (plan.nsplit > 1) {
+    part_o = static_cast<float*>(ws);
+    part_lse = part_o + (size_t)a.T * plan.nsplit * a.H * kMlaDv;
+  }
+  const int64_t gx = (int64_t)a.T * plan.nsplit;
+  const int gy = (a.H + kMlaHeadsPerWg - 1) / kMlaHeadsPerWg;
+  if (gx > 0x7fffffffLL || gy > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sparse_mla_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kMlaThreads), 0, s, a, plan.nsplit,
+                     plan.keys_per_split, part_o, part_lse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.nsplit == 1) return e;
+  hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3((unsigned)a.T, (unsigned)a.H), dim3(kMlaDv / 4), 0, s, a,
+                     plan.nsplit, part_o, part_lse);
+  return hipGetLastError();
+}
+
+}  // namespace fp8idx

@@ -304,6 +304,46 @@ FP8IDX_API fp8idx_status indexer_prepare_decode(const int32_t* seq_len, const in
                                                 int32_t* row_len, int32_t* block_table, int32_t max_pages,
                                                 void* stream);
 
+/*
+ * Sparse MLA attention over the top-k slots: the step after the indexer on
+ * the vessl-ai/sglang PR #87 page (sparse MLA prefill / decode kernels over an
+ * MLA KV pool kept in fp8 e4m3 and widened to bf16 inside the kernel, with
+ * few-token decode run as split-K partials plus a combine).  The page does
+ * not write the attention out; this is softmax attention of every query
+ * token over the pool rows its top-k list selects.  For token t, head h and
+ * the valid slots j of indices[t, 0:topk] (0 <= j < num_slots; other entries,
+ * such as the -1 padding of the top-k output, are skipped, and a repeated
+ * slot counts each time):
+ *
+ *   s_j     = sm_scale * dot(q[t, h, :], kv_scale[j] * e4m3(kv[j, :]))   (all 576 values)
+ *   out[t, h, :] = sum_j softmax(s)_j * kv_scale[j] * e4m3(kv[j, 0:512])  (the latent values)
+ *   lse[t, h]    = log sum_j exp(s_j)
+ *
+ * A token with no valid slot gets out = 0 and lse = -inf.
+ *   q        [T, H, 576] bf16 (uint16 bit patterns), 16-byte aligned
+ *   kv       [num_slots, 576] e4m3fn codes, 16-byte aligned; num_slots >= 1
+ *   kv_scale [num_slots] float32, kv_scale >= 0 (the value weights fold it in)
+ *   indices  [T, ld_indices] int32 slot ids, ld_indices >= topk
+ *   out      [T, H, 512] float32 output, 16-byte aligned
+ *   lse      [T, H] float32 output, or NULL
+ *   ws       fp8idx_sparse_mla_workspace_bytes(T, H, topk) bytes of device
+ *            scratch, 256-byte aligned (NULL allowed when that is 0)
+ * D must be 576, Dv 512 and H a multiple of 16 (else FP8IDX_EUNSUPPORTED);
+ * 1 <= topk.  q is rounded nowhere: the scores use its bf16 values, the fp8
+ * rows widened exactly, and fp32 accumulation; the probabilities enter the
+ * value product in bf16.  T == 0 is a no-op.  Allocates nothing; runs on
+ * `stream`.
+ */
+FP8IDX_API fp8idx_status indexer_sparse_mla(const uint16_t* q, const uint8_t* kv, const float* kv_scale,
+                                            int64_t num_slots, const int32_t* indices, int64_t ld_indices,
+                                            int32_t T, int32_t H, int32_t D, int32_t Dv, int32_t topk,
+                                            float sm_scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                                            void* stream);
+
+/* Bytes of workspace indexer_sparse_mla needs (0 when it runs without
+ * splitting the top-k lists).  Pure host arithmetic. */
+FP8IDX_API size_t fp8idx_sparse_mla_workspace_bytes(int32_t T, int32_t H, int32_t topk);
+
 /* Bytes of device workspace an operation needs (0 when it needs none).
  * rows = logits rows (m or B * next_n), width = keys per row (n or the
  * paged width).  Pure host arithmetic. */

@@ -34,7 +34,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.EXPORTED) == names
@@ -222,3 +222,41 @@ def test_prepare_validation(lib):
     assert g(*bad) == EINVAL                               # table rows shorter than max_pages
     bad = list(okd); bad[5] = 0
     assert g(*bad) == OK
+
+
+def test_sparse_mla_validation(lib):
+    f = lib.indexer_sparse_mla
+    #      q  kv sc  S    idx  ld  T  H   D    Dv  topk scale out lse ws   wsb  stream
+    ok = [P, P, P, 1000, P, 64, 4, 64, 576, 512, 64, 0.1, P, P, None, 0, None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["q", "kv", "sc", "S", "idx", "ld", "T", "H", "D", "Dv", "topk", "scale", "out", "lse", "ws",
+                 "wsb", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    need = lib.fp8idx_sparse_mla_workspace_bytes(4, 64, 64)
+    assert need == 0                              # 4 tokens x 1 step of 64 keys: nothing to split
+    assert call() == EDEV
+    assert call(D=128) == EUNSUP and call(Dv=576) == EUNSUP
+    assert call(H=24) == EUNSUP and call(H=0) == EUNSUP
+    assert call(topk=0) == EINVAL
+    assert call(ld=63) == EINVAL                  # ld_indices < topk
+    assert call(S=0) == EINVAL                    # masked keys read slot 0, so the pool must hold one
+    assert call(T=-1) == EINVAL
+    assert call(T=0, q=NULL, kv=NULL, sc=NULL, idx=NULL, out=NULL) == OK
+    assert call(q=NULL) == EINVAL and call(idx=NULL) == EINVAL and call(out=NULL) == EINVAL
+    assert call(q=P + 8) == EINVAL                # q rows are read as 16-byte vectors
+    assert call(out=P + 4) == EINVAL
+    assert call(lse=P + 2) == EINVAL
+    assert call(lse=NULL) == EDEV                 # lse is optional
+    # few tokens split their lists: partial outputs of 513 floats per (token, split, head)
+    need = lib.fp8idx_sparse_mla_workspace_bytes(2, 64, 2048)
+    nsplit = 32                                   # 2048 keys in 64-key steps, 2 token groups -> 32 splits
+    assert need == 2 * nsplit * 64 * 513 * 4 + 256
+    assert call(T=2, topk=2048, ld=2048) == EWS
+    assert call(T=2, topk=2048, ld=2048, ws=P + 16, wsb=need) == EINVAL   # 256-byte alignment
+    assert call(T=2, topk=2048, ld=2048, ws=P, wsb=need) == EDEV
+    assert lib.fp8idx_sparse_mla_workspace_bytes(256, 64, 2048) == 0     # one workgroup per token already

@@ -281,3 +281,66 @@ CONFIGS: Dict[str, Callable[[], object]] = {
 
 def config_inputs(name: str):
     return CONFIGS[name]()
+
+
+# ---------------------------------------------------------------------------
+# Sparse MLA attention over the top-k slots (the step after the indexer)
+# ---------------------------------------------------------------------------
+
+MLA_DQK = 576   # KV row: 512 latent values + 64 rotary values
+MLA_DV = 512
+
+
+@dataclasses.dataclass
+class SparseMlaInputs:
+    """Sparse MLA inputs: bf16 queries, an fp8 KV pool with per-slot scales, top-k slot lists."""
+
+    name: str
+    q_bits: np.ndarray      # uint16 [T, H, 576], bf16 bit patterns
+    kv_codes: np.ndarray    # uint8 [S, 576], e4m3fn codes
+    kv_scale: np.ndarray    # float32 [S]
+    indices: np.ndarray     # int32 [T, topk]; -1 = no slot
+    sm_scale: float
+
+    @property
+    def T(self) -> int:
+        return int(self.q_bits.shape[0])
+
+    @property
+    def H(self) -> int:
+        return int(self.q_bits.shape[1])
+
+    @property
+    def topk(self) -> int:
+        return int(self.indices.shape[1])
+
+
+def sparse_mla_inputs(T: int, H: int, S: int, topk: int, seed: int, *, invalid_tail: int = 0,
+                      duplicates: int = 0, q_clamp: float = 2.0, kv_clamp: float = 2.0,
+                      sm_scale: Optional[float] = None, name: str = "sparse_mla") -> SparseMlaInputs:
+    """Draw order: q randn [T, H, 576] clamped to [-q_clamp, q_clamp] and rounded to bf16, the KV
+    codes randn [S, 576] clamped and cast to e4m3fn, kv_scale ~ U[0.5, 1.5), then per token a
+    random choice of `topk` distinct slots (without replacement while S allows).  The last
+    `invalid_tail` entries of each list become -1 (the top-k stage's padding) and `duplicates`
+    entries repeat an earlier slot of the same list.  sm_scale defaults to 1 / sqrt(576)."""
+    g = torch.Generator().manual_seed(int(seed))
+    q = torch.randn((T, H, MLA_DQK), generator=g).clamp_(-q_clamp, q_clamp).to(torch.bfloat16)
+    q_bits = q.view(torch.int16).numpy().astype(np.uint16)
+    kv = _randn_fp8(g, (S, MLA_DQK), clamp=kv_clamp, chunk_rows=65536)
+    kv_scale = (torch.rand(S, generator=g) + 0.5).numpy().astype(np.float32)
+    idx = np.empty((T, topk), dtype=np.int32)
+    for t in range(T):
+        if topk <= S:
+            idx[t] = torch.randperm(S, generator=g)[:topk].numpy()
+        else:
+            idx[t] = torch.randint(0, S, (topk,), generator=g).numpy()
+    if duplicates > 0:
+        for t in range(T):
+            pos = torch.randint(1, topk, (duplicates,), generator=g).numpy()
+            src = torch.randint(0, topk, (duplicates,), generator=g).numpy()
+            idx[t, pos] = idx[t, np.minimum(src, pos - 1)]
+    if invalid_tail > 0:
+        idx[:, topk - invalid_tail:] = -1
+    scale = float(1.0 / np.sqrt(MLA_DQK)) if sm_scale is None else float(sm_scale)
+    return SparseMlaInputs(name=name, q_bits=q_bits, kv_codes=kv, kv_scale=kv_scale, indices=idx,
+                           sm_scale=scale)
