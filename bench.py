@@ -62,6 +62,8 @@ def _args():
     ap.add_argument("--overlap", action="store_true", help="time the fused loop serial vs overlapped")
     ap.add_argument("--prep", action="store_true", help="time index preparation at the PR page's shapes")
     ap.add_argument("--quant", action="store_true", help="time the fp8 quantiser on the path's kv and q shapes")
+    ap.add_argument("--sparse-mla", action="store_true",
+                    help="time the sparse MLA attention over top-k slots (the step after the indexer)")
     return ap.parse_args()
 
 
@@ -335,6 +337,77 @@ def quant_workloads(steps, warmup):
     return out
 
 
+# Sparse MLA attention over the top-k slots (the step after the indexer).  The pool holds one MLA
+# row per indexer token slot: 64 requests x E[ctx] = 69632 tokens for the decode workload.
+MLA_SHAPES = (
+    ("decode_t256_h64", 256, 64, 2048, 64 * 69632),     # 64 requests x 4 rows, 64 heads per rank
+    ("decode_t256_h16", 256, 16, 2048, 64 * 69632),     # the same with heads sliced across ranks
+    ("decode_t4_h64_split", 4, 64, 2048, 64 * 69632),   # one request: split-K partials + combine
+    ("prefill_t2048_h64", 2048, 64, 2048, 8 * 65536),   # a prefill batch of 2048 query tokens
+)
+BF16_PEAK = 2.5e15
+
+
+def _mla_device_inputs(T, H, topk, S, seed):
+    """Seeded synthetic sparse MLA inputs drawn on the device (the recipe of
+    workloads.generate.sparse_mla_inputs at pool sizes too large to draw on the host): q randn
+    clamped to [-2, 2] in bf16, kv randn clamped and cast to e4m3fn, kv_scale U[0.5, 1.5), and
+    uniform random slot ids."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    q = torch.randn((T, H, 576), generator=g, device="cuda").clamp_(-2, 2).to(torch.bfloat16)
+    kv = torch.empty((S, 576), dtype=torch.uint8, device="cuda")
+    for s0 in range(0, S, 262144):
+        e = min(S, s0 + 262144)
+        x = torch.randn((e - s0, 576), generator=g, device="cuda").clamp_(-2, 2)
+        kv[s0:e] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+        del x
+    sc = torch.rand(S, generator=g, device="cuda") + 0.5
+    idx = torch.randint(0, S, (T, topk), generator=g, device="cuda", dtype=torch.int32)
+    return q, kv, sc, idx
+
+
+def sparse_mla_workloads(steps, warmup, cpu_tokens=0):
+    """Time indexer_sparse_mla: flops 2 T H topk (576 + 512); HBM bytes = the gathered rows
+    (576 code bytes + a 4-byte scale per listed slot) + q + indices + outputs."""
+    import torch
+    import fp8_mqa_logits_amd as F
+    out = []
+    for name, T, Hh, topk, S in MLA_SHAPES:
+        q, kv, sc, idx = _mla_device_inputs(T, Hh, topk, S, seed=T + Hh)
+        o = torch.empty((T, Hh, 512), dtype=torch.float32, device="cuda")
+        lse = torch.empty((T, Hh), dtype=torch.float32, device="cuda")
+        need = F.fp8idx_sparse_mla_workspace_bytes(T, Hh, topk)
+        ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda") if need else None
+        scale = 576 ** -0.5
+        ms = _event_ms(lambda: F.indexer_sparse_mla(q, kv, sc, idx, scale, out=o, lse=lse, workspace=ws),
+                       steps, warmup)
+        flops = 2.0 * T * Hh * topk * (576 + 512)
+        nbytes = T * topk * (576 + 4) + T * Hh * 576 * 2 + T * topk * 4 + T * Hh * (512 + 1) * 4
+        r = {"workload": f"sparse_mla_{name}", "T": T, "H": Hh, "topk": topk, "slots": S, "ms": ms,
+             "tflops": flops / (ms * 1e-3) / 1e12, "bf16_frac": flops / (ms * 1e-3) / BF16_PEAK,
+             "hbm_bytes": nbytes, "gbps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / HBM_PEAK,
+             "splits": 1 if need == 0 else None}
+        if cpu_tokens > 0 and name == MLA_SHAPES[0][0]:
+            from oracle import sparse_mla
+            import numpy as np
+            toks = list(range(cpu_tokens))
+            sel = idx[:cpu_tokens].cpu().numpy()
+            uniq, inv = np.unique(sel, return_inverse=True)
+            kv_s = kv[torch.from_numpy(uniq).cuda().long()].cpu().numpy()
+            sc_s = sc[torch.from_numpy(uniq).cuda().long()].cpu().numpy()
+            q_s = q[:cpu_tokens].view(torch.int16).cpu().numpy().view(np.uint16)
+            t0 = time.perf_counter()
+            sparse_mla(q_s, kv_s, sc_s, inv.reshape(sel.shape).astype(np.int32), scale, tokens=toks)
+            cpu_s = time.perf_counter() - t0
+            r["cpu_oracle_ms_per_token"] = cpu_s * 1e3 / cpu_tokens
+            r["cpu_oracle_sample"] = f"{cpu_tokens} tokens of {T}, all {Hh} heads, float64 numpy"
+        out.append(r)
+        del q, kv, sc, idx, o, lse, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def _event_ms(fn, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -445,7 +518,8 @@ def main():
             print(json.dumps(r), file=sys.stderr, flush=True)
             del inp, step
             torch.cuda.empty_cache()
-        for q in quant_workloads(a.steps, a.warmup) + prep_workloads(a.steps, a.warmup):
+        for q in (quant_workloads(a.steps, a.warmup) + prep_workloads(a.steps, a.warmup) +
+                  sparse_mla_workloads(a.steps, a.warmup, cpu_tokens=2)):
             rows.append(q)
             print(json.dumps(q), file=sys.stderr, flush=True)
         with open(a.all_workloads, "w") as f:
@@ -473,6 +547,10 @@ def main():
         return
     if a.quant:
         for q in quant_workloads(a.steps, a.warmup):
+            print(json.dumps(q), flush=True)
+        return
+    if a.sparse_mla:
+        for q in sparse_mla_workloads(a.steps, a.warmup, cpu_tokens=0 if a.no_cpu_baseline else 2):
             print(json.dumps(q), flush=True)
         return
 

@@ -20,8 +20,9 @@
 //   contiguous per latent dimension, for the value product).  Each thread
 //   gathers two 16-byte latent chunks of 4 keys and one rotary chunk, and
 //   transposes its 4 x 4 byte tiles with byte permutes while storing, so no
-//   extra LDS pass is needed.  The gather for step i + 2 is in flight while
-//   step i is computed.
+//   extra LDS pass is needed.  The split's slot ids are read into LDS once, so
+//   a gather never waits on an id load; the gather of step i + 2 is in flight
+//   while step i is computed.
 // - Scores are computed transposed, S^T = K Q^T (16x16x32 bf16 MFMA, fp8
 //   widened to bf16 exactly at operand load): a lane then holds 4 consecutive
 //   keys of one head, which is exactly the A-operand layout of P in P V, so
@@ -52,12 +53,22 @@ constexpr int kVTiles = kMlaDv / 16;          // 32 output tiles of 16 values
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;                 // log2 slack before the running maximum moves
+constexpr int kMlaMaxSplitKeys = 2048;        // slot ids of one split held in LDS
 
 struct MlaStage {
   uint8_t k[2][kKBytes];
   uint8_t vt[2][kVtBytes];
   float mul[2][kMlaBlock];   // sm_scale * log2(e) * kv_scale; NaN marks a masked key
   float vsc[2][kMlaBlock];   // kv_scale; 0 for a masked key
+  int32_t idx[kMlaMaxSplitKeys];   // the split's slot ids (-1 past its end)
+};
+
+// One step's gather held in registers by one thread.
+struct MlaGather {
+  v4i lat[4][2];   // two 16-byte latent chunks of each key of the thread's quad
+  v4i rot;         // one rotary chunk
+  float scale;
+  bool ok;
 };
 // 8 e4m3fn bytes (w0 bytes 0..3, then w1 bytes 0..3) -> 8 bf16, exactly.
 __device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
@@ -121,33 +132,30 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
   const int sc = tid & 15;            // latent chunks sc and sc + 16 (16 values each)
   const int rk = tid >> 2;            // rotary: key rk, chunk 32 + (tid & 3)
   const int rc = 32 + (tid & 3);
-  v4i st_lat[4][2];
-  v4i st_rot;
-  float st_scale = 0.f;
-  bool st_ok = false;
   // Every load is unconditional: a masked key (past the range, or an invalid
   // slot) reads slot 0 and is masked by its scale entry.
   auto slot_of = [&](int blk, int key, bool& ok) -> int64_t {
-    const int kk = k_begin + blk * kMlaBlock + key;
-    const int32_t j = kk < k_end ? idx_row[kk] : -1;
+    const int32_t j = sh.idx[blk * kMlaBlock + key];
     ok = j >= 0 && (int64_t)j < a.num_slots;
     return ok ? (int64_t)j : 0;
   };
-  auto stage_load = [&](int blk) {
+  auto stage_load = [&](int blk, MlaGather& st) {
     bool ok;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const uint8_t* row = a.kv + slot_of(blk, 4 * sq + q4, ok) * kMlaDqk;
-      st_lat[q4][0] = *reinterpret_cast<const v4i*>(row + 16 * sc);
-      st_lat[q4][1] = *reinterpret_cast<const v4i*>(row + 16 * (sc + 16));
+      st.lat[q4][0] = *reinterpret_cast<const v4i*>(row + 16 * sc);
+      st.lat[q4][1] = *reinterpret_cast<const v4i*>(row + 16 * (sc + 16));
     }
-    st_rot = *reinterpret_cast<const v4i*>(a.kv + slot_of(blk, rk, ok) * kMlaDqk + 16 * rc);
+    st.rot = *reinterpret_cast<const v4i*>(a.kv + slot_of(blk, rk, ok) * kMlaDqk + 16 * rc);
+    st.ok = false;
+    st.scale = 0.f;
     if (tid < kMlaBlock) {
-      const int64_t j = slot_of(blk, tid, st_ok);
-      st_scale = a.kv_scale[j];
+      const int64_t j = slot_of(blk, tid, st.ok);
+      st.scale = a.kv_scale[j];
     }
   };
-  auto stage_store = [&](int buf) {
+  auto stage_store = [&](int buf, const MlaGather& st) {
     uint8_t* K = sh.k[buf];
     uint8_t* Vt = sh.vt[buf];
     // rows are 8-byte aligned (584-byte stride), so 16-byte chunks go out as two 8-byte stores
@@ -157,17 +165,17 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
     };
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      put16(K + (4 * sq + q4) * kKRow + 16 * sc, st_lat[q4][0]);
-      put16(K + (4 * sq + q4) * kKRow + 16 * (sc + 16), st_lat[q4][1]);
+      put16(K + (4 * sq + q4) * kKRow + 16 * sc, st.lat[q4][0]);
+      put16(K + (4 * sq + q4) * kKRow + 16 * (sc + 16), st.lat[q4][1]);
     }
-    put16(K + rk * kKRow + 16 * rc, st_rot);
+    put16(K + rk * kKRow + 16 * rc, st.rot);
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
       const int chunk = sc + 16 * ch;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t x[4] = {(uint32_t)st_lat[0][ch][w], (uint32_t)st_lat[1][ch][w], (uint32_t)st_lat[2][ch][w],
-                               (uint32_t)st_lat[3][ch][w]};
+        const uint32_t x[4] = {(uint32_t)st.lat[0][ch][w], (uint32_t)st.lat[1][ch][w], (uint32_t)st.lat[2][ch][w],
+                               (uint32_t)st.lat[3][ch][w]};
         uint32_t y[4];
         transpose4x4(x, y);
 #pragma unroll
@@ -176,10 +184,17 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
       }
     }
     if (tid < kMlaBlock) {
-      sh.mul[buf][tid] = st_ok ? a.sm_scale * kLog2e * st_scale : __builtin_nanf("");
-      sh.vsc[buf][tid] = st_ok ? st_scale : 0.f;
+      sh.mul[buf][tid] = st.ok ? a.sm_scale * kLog2e * st.scale : __builtin_nanf("");
+      sh.vsc[buf][tid] = st.ok ? st.scale : 0.f;
     }
   };
+
+  // the split's slot ids, padded with -1 to whole steps
+  for (int i = tid; i < nblk * kMlaBlock; i += kMlaThreads) {
+    const int kk = k_begin + i;
+    sh.idx[i] = kk < k_end ? idx_row[kk] : -1;
+  }
+  __syncthreads();
 
   // ---- online softmax state (head l16; equal in the 4 lane groups) and output
   float mrun = -INFINITY;
@@ -188,15 +203,8 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
 #pragma unroll
   for (int n = 0; n < kVTiles; ++n) O[n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  if (nblk > 0) {
-    stage_load(0);
-    stage_store(0);
-    if (nblk > 1) stage_load(1);
-  }
-  __syncthreads();
-
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int cb = blk & 1;
+  // One step of scores, softmax and value product on LDS buffer cb.
+  auto compute = [&](int cb) {
     const uint8_t* K = sh.k[cb];
     const uint8_t* Vt = sh.vt[cb];
 
@@ -271,9 +279,21 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
       }
     }
 
-    // stage step blk + 1 into the other buffer (its loads were issued a step ago) and load step blk + 2
-    if (blk + 1 < nblk) stage_store(cb ^ 1);
-    if (blk + 2 < nblk) stage_load(blk + 2);
+  };
+
+  // Step i sits in LDS buffer i & 1; the gather of step i + 2 is in flight in
+  // registers while step i is computed.
+  MlaGather ga;
+  if (nblk > 0) {
+    stage_load(0, ga);
+    stage_store(0, ga);
+  }
+  if (nblk > 1) stage_load(1, ga);
+  __syncthreads();
+  for (int blk = 0; blk < nblk; ++blk) {
+    compute(blk & 1);
+    if (blk + 1 < nblk) stage_store((blk + 1) & 1, ga);
+    if (blk + 2 < nblk) stage_load(blk + 2, ga);
     __syncthreads();
   }
 
@@ -327,8 +347,9 @@ __global__ __launch_bounds__(128) void sparse_mla_combine_kernel(SparseMlaArgs a
 }
 
 // Splits each top-k list so that about kMlaTargetWgs workgroups run (one per
-// CU of the 256-CU part), never below one 64-key step per split.  A pure
-// function of the shape, so the workspace size needs no device.
+// CU of the 256-CU part), never below one 64-key step and never above the
+// 2048 slot ids a workgroup holds in LDS.  A pure function of the shape, so
+// the workspace size needs no device.
 constexpr int64_t kMlaTargetWgs = 256;
 
 SparseMlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t topk) {
@@ -336,7 +357,8 @@ SparseMlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t topk) {
   const int64_t blocks = std::max<int64_t>(1, ((int64_t)topk + kMlaBlock - 1) / kMlaBlock);
   const int64_t groups = std::max<int64_t>(1, (int64_t)T * ((H + kMlaHeadsPerWg - 1) / kMlaHeadsPerWg));
   int64_t nsplit = std::min<int64_t>(blocks, std::max<int64_t>(1, (kMlaTargetWgs + groups - 1) / groups));
-  const int64_t blocks_per_split = (blocks + nsplit - 1) / nsplit;
+  const int64_t blocks_per_split =
+      std::min<int64_t>((blocks + nsplit - 1) / nsplit, kMlaMaxSplitKeys / kMlaBlock);
   nsplit = (blocks + blocks_per_split - 1) / blocks_per_split;
   p.nsplit = (int32_t)nsplit;
   p.keys_per_split = (int32_t)(blocks_per_split * kMlaBlock);
