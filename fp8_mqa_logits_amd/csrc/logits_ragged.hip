@@ -230,8 +230,8 @@ hipError_t launch_logits_ragged(const RaggedLogitsArgs& a, const DeviceInfo& dev
   int64_t resident = (int64_t)(dev.cu_count > 0 ? dev.cu_count : 256) * per_cu;
   if (resident >= 8) resident = resident / 8 * 8;
   // key splits: multiples of 8 (one residue per XCD), doubled until there are
-  // about 8 items per resident workgroup, keeping >= 1024 keys per split
-  const int64_t max_splits = std::max<int64_t>(1, a.n / 1024);
+  // about 8 items per resident workgroup, keeping >= 128 keys (2 tiles) per split
+  const int64_t max_splits = std::max<int64_t>(1, a.n / 128);
   int64_t splits = std::min<int64_t>(8, max_splits);
   while (splits * 2 <= max_splits && row_blocks * splits < 8 * resident) splits *= 2;
   int64_t kps = (a.n + splits - 1) / splits;
