@@ -89,35 +89,6 @@ __device__ __forceinline__ int unit_pages(const PagedLogitsArgs& a, int qgroups,
   return (unit_at(a, qgroups, u).lmax + kPage - 1) / kPage;
 }
 
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
-  return x;
-}
-
-__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  return x;
-}
-
-__device__ __forceinline__ int64_t uniform64(int64_t x) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
-// Equal split of `total` items over `parts`: part i gets [first, first + count).
-__device__ __forceinline__ void split_range(int64_t total, int64_t parts, int64_t i, int64_t& first,
-                                            int64_t& count) {
-  const int64_t base = total / parts, rem = total - base * parts;
-  first = i * base + min(i, rem);
-  count = base + (i < rem ? 1 : 0);
-}
-
 template <int DEPTH>
 __global__ __launch_bounds__(64 * kPagedWaves, 2) void logits_paged_kernel(PagedLogitsArgs a, int qgroups) {
   const int lane = threadIdx.x & 63;

@@ -9,11 +9,16 @@
 // - Work items are (block of kRows = 4 * WAVES consecutive query rows, slice
 //   of the keys); each wave of a workgroup owns 4 of the item's rows, whose
 //   q (4 rows x 32 heads x 128 bytes) stays in VGPRs as eight 16x16x128 MFMA
-//   A-operands next to the matching weights.  The grid holds only as many
-//   workgroups as are resident at once and each loops over items, so the
-//   last round is never mostly empty; splits come in multiples of 8 so a
-//   workgroup (and its XCD, blocks being dealt to the 8 XCDs round-robin)
-//   keeps streaming the same kv slice, which then stays in that XCD's L2.
+//   A-operands next to the matching weights.
+// - The grid holds only as many workgroups as are resident at once.  The
+//   items' 64-key tiles, laid end to end in split-major order, are divided
+//   into equal contiguous ranges, one per workgroup, which each workgroup
+//   finds by itself from ks/ke (a prefix scan over the row blocks' windows),
+//   so no host schedule or workspace is needed.  Windows that differ between
+//   rows (the causal triangle) therefore do not leave some workgroups with
+//   more tiles than others.  Workgroups are dealt to the 8 XCDs round-robin;
+//   ranks are assigned XCD-major, so each XCD covers one contiguous eighth of
+//   the order, about one kv slice, which stays in its L2.
 // - Keys stream through LDS in tiles of 64 keys x 128 bytes (8 KiB, double
 //   buffered), loaded with coalesced 16-byte global loads.  Inside a row the
 //   16-byte chunks are XOR-swizzled by (key & 7) so that the B-operand reads
@@ -35,14 +40,81 @@
 #include "mqa_core.hpp"
 
 #include <algorithm>
+#include <mutex>
 
 namespace fp8idx {
 
 constexpr int kTileKeys = 64;
+constexpr int kQueueSlots = 64;   // streams with a slot of their own
+
+// Work-queue counters: per slot, one claim counter per XCD queue and a count of finished
+// workgroups.  The last workgroup of a launch resets its slot, so the next launch on the slot
+// starts from zero.  Slots belong to streams: launches on one stream never overlap.
+__device__ unsigned int g_ragged_queue[kQueueSlots][16];
+
+// Tiles of one item: row block with key window union [lo, hi), split [split_lo, split_hi).
+struct ItemGeom {
+  int tile_lo, tile_end, ntiles;
+};
+
+__device__ __forceinline__ ItemGeom item_geom(int lo, int hi, int split_lo, int split_hi) {
+  ItemGeom g{split_lo, split_lo, 0};
+  const int klo = max(lo, split_lo), khi = min(hi, split_hi);
+  if (klo < khi) {
+    g.tile_lo = max(split_lo, klo & ~(kTileKeys - 1));
+    g.ntiles = (khi - g.tile_lo + kTileKeys - 1) / kTileKeys;
+    g.tile_end = min(split_hi, g.tile_lo + g.ntiles * kTileKeys);
+  }
+  return g;
+}
+
+constexpr unsigned int kNoItem = 0xffffffffu;
+
+// Splits served by queue x: x, x + 8, x + 16, ... below `splits`.
+__device__ __forceinline__ int queue_splits(int splits, int x) { return splits > x ? (splits - x + 7) / 8 : 0; }
+
+// Workgroups whose fixed first item comes from queue x (those with blockIdx % 8 == x).
+__device__ __forceinline__ unsigned int queue_fixed(int x) { return (gridDim.x + 7u - (unsigned int)x) / 8u; }
+
+// Items of queue x.
+__device__ __forceinline__ unsigned int queue_items(int splits, int row_blocks, int x) {
+  return (unsigned int)(queue_splits(splits, x) * row_blocks);
+}
+
+// Next item of a workgroup as (index in queue) * 8 + queue, or kNoItem once every queue is empty.
+// `state` (thread 0's own) is 0 before the fixed first item, 1 while the home queue may hold items,
+// 2 after it ran out.  Other queues are probed by reading their counters first: counters only
+// grow, so one read at or past a queue's end proves that queue empty.
+__device__ __forceinline__ unsigned int claim_item(unsigned int* queue, int home, int& state, int splits,
+                                                   int row_blocks) {
+  const unsigned int home_items = queue_items(splits, row_blocks, home);
+  if (state == 0) {
+    state = 1;
+    const unsigned int c = blockIdx.x >> 3;
+    if (c < home_items) return c * 8u + (unsigned int)home;
+  }
+  if (state == 1) {
+    const unsigned int c = atomicAdd(&queue[home], 1u) + queue_fixed(home);
+    if (c < home_items) return c * 8u + (unsigned int)home;
+    state = 2;
+  }
+  for (;;) {
+    int pick = -1;
+#pragma unroll
+    for (int d = 1; d < 8; ++d) {
+      const int x = (home + d) & 7;
+      const unsigned int taken = __hip_atomic_load(&queue[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (pick < 0 && taken + queue_fixed(x) < queue_items(splits, row_blocks, x)) pick = x;
+    }
+    if (pick < 0) return kNoItem;
+    const unsigned int c = atomicAdd(&queue[pick], 1u) + queue_fixed(pick);
+    if (c < queue_items(splits, row_blocks, pick)) return c * 8u + (unsigned int)pick;
+  }
+}
 
 template <int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogitsArgs a, int splits,
-                                                                       int keys_per_split, int items) {
+__global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogitsArgs a, int splits, int kps,
+                                                                       int slot) {
   constexpr int kThreads = 64 * WAVES;
   constexpr int kRows = 4 * WAVES;
   constexpr int kChunks = kTileKeys * (kDim / 16);   // 16-byte chunks per tile
@@ -53,21 +125,45 @@ __global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogi
   __shared__ float s_scale[2][kTileKeys];
   __shared__ int s_ks[kRows];
   __shared__ int s_ke[kRows];
+  __shared__ unsigned int s_claim;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = a.n;
   const bool clean = a.clean != 0;
+  const int row_blocks = (a.m + kRows - 1) / kRows;
+  unsigned int* const queue = g_ragged_queue[slot];
 
-  // Persistent loop over (row block, key split) items.  The grid is a
-  // multiple of 8 and so is `splits` on large problems, so a workgroup keeps
-  // the same split residue, i.e. the same XCD streams the same kv slice.
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int rb = item / splits;
-    const int split = item - rb * splits;
+  // Queue x holds the items of the splits x, x + 8, x + 16, ...: row blocks from the last (the
+  // longest causal windows) to the first, each with all of the queue's splits.  Workgroups are
+  // dealt to the 8 XCDs round-robin, so queue blockIdx % 8 is served by one XCD, whose L2 keeps
+  // those kv slices.  A workgroup's first item is fixed (item blockIdx / 8 of its queue); the
+  // counters hand out the rest.  A workgroup whose queue is empty moves on
+  // to a queue that is not.
+  const int home = blockIdx.x & 7;
+  // When the fixed first items cover every queue, the counters are not needed at all.
+  bool fixed_only = true;
+#pragma unroll
+  for (int x = 0; x < 8; ++x)
+    fixed_only = fixed_only && queue_items(splits, row_blocks, x) <= queue_fixed(x);
+  int claim_state = 0;
+  for (;;) {
+    __syncthreads();   // the previous item is done with s_ks/s_ke, the tiles and s_claim
+    if (tid == 0) {
+      s_claim = fixed_only && claim_state > 0 ? kNoItem : claim_item(queue, home, claim_state, splits, row_blocks);
+    }
+    __syncthreads();
+    const unsigned int claim = s_claim;
+    if (claim == kNoItem) break;
+    const int xq = (int)(claim & 7u);
+    const int nsx = queue_splits(splits, xq);
+    const unsigned int c = claim >> 3;
+    const int rb = row_blocks - 1 - (int)(c / (unsigned int)nsx);
+    const int split = xq + 8 * (int)(c % (unsigned int)nsx);
     const int row0 = rb * kRows;
-    __syncthreads();   // the previous item is done with s_ks/s_ke and the kv tiles
+    const int split_lo = split * kps;
+    const int split_hi = n - split_lo < kps ? n : split_lo + kps;
 
     if (tid < kRows) {
       const int r = row0 + tid;
@@ -90,17 +186,8 @@ __global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogi
         hi = max(hi, e);
       }
     }
-    const int split_lo = split * keys_per_split;
-    const int split_hi = min(n, split_lo + keys_per_split);
-    const int klo = max(lo, split_lo);
-    const int khi = min(hi, split_hi);
-    int tile_lo = split_lo, tile_end = split_lo;   // computed range [tile_lo, tile_end)
-    int ntiles = 0;
-    if (klo < khi) {
-      tile_lo = max(split_lo, klo & ~(kTileKeys - 1));
-      ntiles = (khi - tile_lo + kTileKeys - 1) / kTileKeys;
-      tile_end = min(split_hi, tile_lo + ntiles * kTileKeys);
-    }
+    const ItemGeom geo = item_geom(lo, hi, split_lo, split_hi);
+    const int tile_lo = geo.tile_lo, tile_end = geo.tile_end, ntiles = geo.ntiles;
     const int rows_here = min(kRows, a.m - row0);
 
     if (clean) {
@@ -109,8 +196,8 @@ __global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogi
       const int w1 = split_hi - tile_end;
       for (int r = 0; r < rows_here; ++r) {
         float* out = a.logits + (int64_t)(row0 + r) * a.ld;
-        for (int c = tid; c < w0; c += kThreads) out[split_lo + c] = -INFINITY;
-        for (int c = tid; c < w1; c += kThreads) out[tile_end + c] = -INFINITY;
+        for (int c2 = tid; c2 < w0; c2 += kThreads) out[split_lo + c2] = -INFINITY;
+        for (int c2 = tid; c2 < w1; c2 += kThreads) out[tile_end + c2] = -INFINITY;
       }
     }
     if (ntiles == 0) continue;
@@ -150,13 +237,13 @@ __global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogi
     float stage_scale = 0.f;
     auto gload = [&](int tile) {
 #pragma unroll
-      for (int c = 0; c < kChunksPerThread; ++c) {
-        const int ci = tid + c * kThreads;
+      for (int c2 = 0; c2 < kChunksPerThread; ++c2) {
+        const int ci = tid + c2 * kThreads;
         const int key = ci >> 3;
         const int j = tile + key;
         v4i v = {0, 0, 0, 0};
         if (j < n) v = *reinterpret_cast<const v4i*>(a.kv + (size_t)j * kDim + (ci & 7) * 16);
-        stage[c] = v;
+        stage[c2] = v;
       }
       if (tid < kTileKeys) {
         const int j = tile + tid;
@@ -165,10 +252,10 @@ __global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogi
     };
     auto lstore = [&](int buf) {
 #pragma unroll
-      for (int c = 0; c < kChunksPerThread; ++c) {
-        const int ci = tid + c * kThreads;
+      for (int c2 = 0; c2 < kChunksPerThread; ++c2) {
+        const int ci = tid + c2 * kThreads;
         const int key = ci >> 3;
-        *reinterpret_cast<v4i*>(&s_kv[buf][key * kDim + (((ci & 7) ^ (key & 7)) * 16)]) = stage[c];
+        *reinterpret_cast<v4i*>(&s_kv[buf][key * kDim + (((ci & 7) ^ (key & 7)) * 16)]) = stage[c2];
       }
       if (tid < kTileKeys) s_scale[buf][tid] = stage_scale;
     };
@@ -211,6 +298,16 @@ __global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogi
       }
     }
   }
+
+  // Every queue is empty for this workgroup.  The last one to get here resets the slot: by then no
+  // workgroup of this launch touches the counters again.  (With fixed items only, none touched them.)
+  if (tid == 0 && !fixed_only) {
+    __threadfence();
+    if (atomicAdd(&queue[8], 1u) == gridDim.x - 1) {
+#pragma unroll
+      for (int i = 0; i < 9; ++i) atomicExch(&queue[i], 0u);
+    }
+  }
 }
 
 void query_ragged_occupancy(DeviceInfo& d) {
@@ -218,6 +315,22 @@ void query_ragged_occupancy(DeviceInfo& d) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, logits_ragged_kernel<4>, 256, 0) != hipSuccess)
     per_cu = 1;
   d.ragged_wgs_per_cu = per_cu > 0 ? per_cu : 1;
+}
+
+// Work-queue slot of a stream: the first kQueueSlots streams get slots of their own; later ones
+// reuse the least recently assigned slot.
+static int queue_slot(hipStream_t s) {
+  static std::mutex mu;
+  static hipStream_t owner[kQueueSlots];
+  static int assigned = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const int used = std::min(assigned, kQueueSlots);
+  for (int i = 0; i < used; ++i)
+    if (owner[i] == s) return i;
+  const int slot = assigned % kQueueSlots;
+  owner[slot] = s;
+  ++assigned;
+  return slot;
 }
 
 hipError_t launch_logits_ragged(const RaggedLogitsArgs& a, const DeviceInfo& dev, hipStream_t s) {
@@ -229,19 +342,20 @@ hipError_t launch_logits_ragged(const RaggedLogitsArgs& a, const DeviceInfo& dev
   const int per_cu = dev.ragged_wgs_per_cu > 0 ? dev.ragged_wgs_per_cu : 1;
   int64_t resident = (int64_t)(dev.cu_count > 0 ? dev.cu_count : 256) * per_cu;
   if (resident >= 8) resident = resident / 8 * 8;
-  // key splits: multiples of 8 (one residue per XCD), doubled until there are
+  // key splits: multiples of 8 (one queue per XCD), doubled until there are
   // about 8 items per resident workgroup, keeping >= 128 keys (2 tiles) per split
   const int64_t max_splits = std::max<int64_t>(1, a.n / 128);
   int64_t splits = std::min<int64_t>(8, max_splits);
   while (splits * 2 <= max_splits && row_blocks * splits < 8 * resident) splits *= 2;
-  int64_t kps = (a.n + splits - 1) / splits;
+  int64_t kps = (std::max<int64_t>(a.n, 1) + splits - 1) / splits;
   kps = (kps + kTileKeys - 1) / kTileKeys * kTileKeys;
-  splits = (a.n + kps - 1) / kps;
+  splits = (std::max<int64_t>(a.n, 1) + kps - 1) / kps;
   const int64_t items = row_blocks * splits;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
   const int64_t grid = std::min<int64_t>(items, resident);
+  const int slot = queue_slot(s);
   hipLaunchKernelGGL(logits_ragged_kernel<kWaves>, dim3((unsigned)grid), dim3(64 * kWaves), 0, s, a,
-                     (int)splits, (int)kps, (int)items);
+                     (int)splits, (int)kps, slot);
   return hipGetLastError();
 }
 

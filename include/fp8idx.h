@@ -118,6 +118,13 @@ typedef enum fp8idx_op {
  *            other columns < n hold unspecified values.  Columns >= n are
  *            never touched.
  * m == 0 is a no-op.  Requires n >= 1, m >= 0.
+ * Workgroups take their items from a device-side work queue that belongs to
+ * the stream (a fixed table of 64 slots per device; each launch resets its
+ * slot when it ends).  Launches on one stream, or replays of a captured
+ * graph on one stream, never overlap and are always safe.  Launches that may
+ * run at the same time must be on different streams; the first 64 streams
+ * of the process get slots of their own, later ones share the least recently
+ * assigned slot.  The same holds for the logits launches of the fused entries.
  */
 FP8IDX_API fp8idx_status indexer_logits_ragged(const uint8_t* q, const uint8_t* kv, const float* kv_scale,
                                     const float* weights, const int32_t* ks, const int32_t* ke,

@@ -47,6 +47,53 @@ def _random_windows(rng, m, n):
     return ks.astype(np.int32), ke.astype(np.int32)
 
 
+def test_ragged_repeats_streams_and_graph_replays():
+    """Workgroups claim items from a per-stream device work queue that each launch resets when it ends:
+    back-to-back launches, launches on two streams at once and graph replays between eager launches
+    must all give the same bytes."""
+    rng = np.random.default_rng(77)
+    ks1, ke1 = _random_windows(rng, 300, 5000)
+    a = ragged_inputs(300, 5000, 8, seed=78, ks=ks1, ke=ke1)
+    b = ragged_inputs(1000, 2100, 8, seed=79)
+    da, db = _ragged_dev(a), _ragged_dev(b)
+    ref_a = F.indexer_logits_ragged(*da, clean=True)
+    ref_b = F.indexer_logits_ragged(*db, clean=True)
+    torch.cuda.synchronize()
+    assert_logits_close(ref_a.cpu().numpy(), mqa_logits(a.q, a.kv, a.kv_scale, a.weights, a.ks, a.ke),
+                        a.ks, a.ke, clean=True, what="queue a")
+    assert_logits_close(ref_b.cpu().numpy(), mqa_logits(b.q, b.kv, b.kv_scale, b.weights, b.ks, b.ke),
+                        b.ks, b.ke, clean=True, what="queue b")
+    for rep in range(3):
+        out = F.indexer_logits_ragged(*da, clean=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_a), f"repeat {rep}"
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    torch.cuda.synchronize()
+    for rep in range(3):
+        with torch.cuda.stream(s1):
+            oa = F.indexer_logits_ragged(*da, clean=True)
+        with torch.cuda.stream(s2):
+            ob = F.indexer_logits_ragged(*db, clean=True)
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    for rep, (oa, ob) in enumerate(outs):
+        assert torch.equal(oa, ref_a) and torch.equal(ob, ref_b), f"two streams, round {rep}"
+    sg = torch.cuda.Stream()
+    static_out = torch.empty_like(ref_a)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=sg):
+        F.indexer_logits_ragged(*da, clean=True, logits=static_out)
+    for rep in range(3):
+        static_out.fill_(7.0)
+        g.replay()
+        eager = F.indexer_logits_ragged(*db, clean=True)
+        torch.cuda.synchronize()
+        assert torch.equal(static_out, ref_a), f"graph replay {rep}"
+        assert torch.equal(eager, ref_b), f"eager launch after replay {rep}"
+
+
 @pytest.mark.parametrize("m,n", [(1, 17), (5, 64), (16, 65), (37, 1000), (50, 3000), (33, 4133)])
 @pytest.mark.parametrize("clean", [True, False])
 def test_ragged_shapes_and_windows(m, n, clean):
