@@ -8,20 +8,21 @@
 //
 // Work decomposition
 // - A unit is (request, group of 4 query rows); it owns ceil(L / 64) pages,
-//   L being the longest of its rows' lengths (clamped to the width).  The
-//   units' pages, laid end to end, are split into equal contiguous ranges,
-//   one per wave of a persistent grid (every resident wave of the device), so
-//   each wave gets the same number of pages whatever the mix of context
-//   lengths: no tail round of half-empty workgroups.  Each wave finds its
-//   first (unit, page) with a wave-wide prefix scan of the units' page counts,
-//   computed from the device-side lengths, so no host schedule or workspace
-//   is needed.  Waves never synchronise with each other.
+//   L being the longest of its rows' lengths (clamped to the width), claimed
+//   in chunks of 4 pages.  The units' chunks, laid end to end, are split into
+//   equal contiguous ranges, one per workgroup of a persistent grid (one
+//   8-wave workgroup per CU), found by each workgroup with a wave-wide prefix
+//   scan of the chunk counts computed from the device-side lengths: no host
+//   schedule or workspace.  Inside a workgroup, waves take chunks from its
+//   range one at a time through an LDS counter.  Every CU gets the same work,
+//   and a wave that its SIMD serves less often (issue favours older waves)
+//   simply takes fewer chunks, so the waves finish together.
 // - A wave holds the 4 query rows of its current unit (q and weights in
-//   VGPRs), reads the page ids of its range with one vector load, and streams
-//   each page's 64 keys x 128 bytes (8 KiB, contiguous) straight from HBM into
-//   four MFMA B-operands, DEPTH pages deep: while one page is scored the next
-//   DEPTH - 1 pages' loads are in flight.  Every kv byte is read once and is
-//   shared by the 4 query rows.
+//   VGPRs, reloaded when the unit changes).  The next chunk is claimed and its
+//   page ids loaded while the current chunk is scored; each page's 64 keys x
+//   128 bytes (8 KiB, contiguous) stream straight from HBM into four MFMA
+//   B-operands one page ahead of the page being scored, across chunk
+//   boundaries.  Every kv byte is read once and is shared by the 4 query rows.
 // - Scoring, ReLU, head weighting and the cross-lane head reduction are the
 //   same register-resident core as the ragged kernel.
 // - With clean set, keys past a unit's scored range are filled with -inf by a
@@ -34,9 +35,10 @@
 namespace fp8idx {
 
 constexpr int kPage = 64;
-constexpr int kPagedWaves = 4;
+constexpr int kPagedWaves = 8;         // one workgroup per CU (2 waves per SIMD)
 constexpr int kPagedDepth = 2;         // pages in flight per wave, the scored one included
-constexpr int kMinPagesPerWave = 4;    // small totals run on fewer waves
+constexpr int kChunk = 4;              // pages a wave claims at a time
+constexpr int kMinChunksPerWg = 2;     // small totals run on fewer workgroups
 constexpr int kFragsPerPage = kPage / 16;   // 16-key MFMA fragments per page
 
 // One page's four B-operands (lane l: key l % 16 of each 16-key fragment,
@@ -84,13 +86,21 @@ __device__ __forceinline__ Unit unit_at(const PagedLogitsArgs& a, int qgroups, i
   return t;
 }
 
-__device__ __forceinline__ int unit_pages(const PagedLogitsArgs& a, int qgroups, int units, int u) {
+// Claimable chunks of unit u: its pages in runs of kChunk (the last run may be shorter).
+__device__ __forceinline__ int unit_chunks(const Unit& t) { return ((t.lmax + kPage - 1) / kPage + kChunk - 1) / kChunk; }
+
+__device__ __forceinline__ int unit_chunks_at(const PagedLogitsArgs& a, int qgroups, int units, int u) {
   if (u >= units) return 0;
-  return (unit_at(a, qgroups, u).lmax + kPage - 1) / kPage;
+  return unit_chunks(unit_at(a, qgroups, u));
 }
 
+static_assert(kPagedDepth == 2, "the chunk loop keeps one page in flight ahead of the scored one");
+static_assert(kChunk % kPagedDepth == 0, "chunks start on the first page buffer");
+
 template <int DEPTH>
-__global__ __launch_bounds__(64 * kPagedWaves, 2) void logits_paged_kernel(PagedLogitsArgs a, int qgroups) {
+__global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(PagedLogitsArgs a, int qgroups) {
+  __shared__ int s_next;   // next chunk of this workgroup's range to hand out
+
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t waves_total = (int64_t)gridDim.x * kPagedWaves;
@@ -99,58 +109,91 @@ __global__ __launch_bounds__(64 * kPagedWaves, 2) void logits_paged_kernel(Paged
   const bool clean = a.clean != 0;
   const int my_q = reduce_rows4_qsel(lane);
 
-  // Total pages over all units (the first 64 units' counts are kept for the search below).
-  int p_first = unit_pages(a, qgroups, units, lane);
-  int64_t total = __builtin_amdgcn_readfirstlane(wave_sum(p_first));
+  // Total chunks over all units (the first 64 units' counts are kept for the search below).
+  const int c_first = unit_chunks_at(a, qgroups, units, lane);
+  int64_t total = __builtin_amdgcn_readfirstlane(wave_sum(c_first));
   for (int c = 64; c < units; c += 64)
-    total += __builtin_amdgcn_readfirstlane(wave_sum(unit_pages(a, qgroups, units, c + lane)));
+    total += __builtin_amdgcn_readfirstlane(wave_sum(unit_chunks_at(a, qgroups, units, c + lane)));
   total = uniform64(total);
 
-  const int64_t nw = min(waves_total, max<int64_t>((total + kMinPagesPerWave - 1) / kMinPagesPerWave, 1));
-  int64_t start = 0, count = 0;
-  if (gw < nw) split_range(total, nw, gw, start, count);
+  // This workgroup's equal share of the chunks.  Its waves take chunks from the share one at a time
+  // through an LDS counter, so a wave that the SIMD serves less often simply takes fewer.
+  const int64_t ng = min((int64_t)gridDim.x, max<int64_t>((total + kMinChunksPerWg - 1) / kMinChunksPerWg, 1));
+  int64_t c0 = 0, ccount = 0;
+  if (blockIdx.x < ng) split_range(total, ng, blockIdx.x, c0, ccount);
+  if (threadIdx.x == 0) s_next = 0;
+  __syncthreads();
 
-  // Locate the unit holding page `start` of the concatenation, and the page within it.
-  int u = 0;
-  int off = 0;
-  if (count > 0) {
+  // Cursor: the unit holding the latest claimed chunk and the index of its first chunk.  Claims of
+  // one wave only grow, so the cursor only moves forward.
+  int cu = 0;
+  int64_t cstart = 0;
+  if (ccount > 0) {
     int64_t run = 0;
     for (int c = 0; c < units; c += 64) {
-      const int p = c == 0 ? p_first : unit_pages(a, qgroups, units, c + lane);
+      const int p = c == 0 ? c_first : unit_chunks_at(a, qgroups, units, c + lane);
       const int incl = wave_inclusive_scan(p, lane);
       const int chunk = __builtin_amdgcn_readlane(incl, 63);
-      if (start - run < chunk) {
-        const int t = (int)(start - run);
+      if (c0 - run < chunk) {
+        const int t = (int)(c0 - run);
         const int first = __builtin_amdgcn_readfirstlane(__builtin_ctzll(ballot64(incl > t)));
-        u = c + first;
-        off = t - (__builtin_amdgcn_readlane(incl, first) - __builtin_amdgcn_readlane(p, first));
+        cu = c + first;
+        cstart = run + __builtin_amdgcn_readlane(incl, first) - __builtin_amdgcn_readlane(p, first);
         break;
       }
       run += chunk;
     }
   }
+  Unit ct = unit_at(a, qgroups, min(cu, units - 1));
+  int ct_chunks = unit_chunks(ct);
 
-  for (int64_t remaining = count; remaining > 0 && u < units; ++u, off = 0) {
-    const Unit t = unit_at(a, qgroups, u);
-    const int pages = (t.lmax + kPage - 1) / kPage;
-    const int n_here = (int)min<int64_t>(pages - off, remaining);
-    remaining -= max(n_here, 0);
-    if (n_here <= 0) continue;
-    const int32_t* __restrict__ bt = a.block_table + (int64_t)t.b * a.max_pages + off;
-    // scored keys of this unit: whole 16-key fragments up to the longest row
-    const int covered = min(a.width, (t.lmax + 15) / 16 * 16);
-    const bool row_ok = my_q < t.nq;
-    const int my_len = t.len[my_q];
-    float* __restrict__ out_row = a.logits + (int64_t)(row_ok ? t.r_base + my_q : 0) * a.ld;
+  // Claims the next chunk: its unit, first page, page count (0: none left) and page ids (lane l:
+  // page l, lanes past the count repeat the last one).  The id load is unconditional (entry 0 of the
+  // table when nothing is left), so every path leaves the same loads in flight, and its value is not
+  // touched here: the wait for it comes where it is used, after the loads issued before it.
+  int nx_u = 0, nx_pg = 0, nx_n = 0;
+  int32_t nx_ids = -1;
+  auto claim = [&]() {
+    int rel = 0;
+    if (lane == 0) rel = atomicAdd(&s_next, 1);
+    rel = __builtin_amdgcn_readfirstlane(rel);
+    int64_t idx = 0;
+    nx_n = 0;
+    if (rel < ccount) {
+      const int64_t c = c0 + rel;
+      while (c >= cstart + ct_chunks) {
+        cstart += ct_chunks;
+        ++cu;
+        ct = unit_at(a, qgroups, cu);
+        ct_chunks = unit_chunks(ct);
+      }
+      nx_u = cu;
+      nx_pg = (int)(c - cstart) * kChunk;
+      nx_n = min(kChunk, (ct.lmax + kPage - 1) / kPage - nx_pg);
+      idx = (int64_t)ct.b * a.max_pages + nx_pg + min(lane, nx_n - 1);
+    }
+    nx_ids = a.block_table[idx];
+  };
 
-    for (int s0 = 0; s0 < n_here; s0 += 64) {
-      const int seg = min(64, n_here - s0);
-      // page ids of this segment, one per lane; loaded before q so q's loads
-      // overlap the wait for them
-      const int32_t pidv = lane < seg ? bt[s0 + lane] : -1;
+  claim();
+  PageFrags buf[DEPTH];
+  load_page(a, nx_n > 0 ? __builtin_amdgcn_readfirstlane(nx_ids) : -1, lane, buf[0]);
+  Unit t{};
+  QFrags qf;
+  int q_u = -1;
+  int covered = 0, my_len = 0;
+  bool row_ok = false;
+  float* __restrict__ out_row = a.logits;
+
+  while (nx_n > 0) {
+    // the claimed chunk becomes the current one; the cursor still sits on its unit
+    const int cur_pg = nx_pg, cur_n = nx_n;
+    const int32_t cur_pidv = lane < cur_n ? nx_ids : -1;
+    if (nx_u != q_u) {
+      q_u = nx_u;
+      t = ct;
       // a unit with fewer than 4 rows repeats its first row in the missing
       // slots (unconditional loads again); those lanes never store
-      QFrags qf;
 #pragma unroll
       for (int qi = 0; qi < 4; ++qi) {
         const int row = qi < t.nq ? t.r_base + qi : t.r_base;
@@ -160,40 +203,45 @@ __global__ __launch_bounds__(64 * kPagedWaves, 2) void logits_paged_kernel(Paged
           qf.w[qi][h] = load_w4(a.weights, row, true, h, lane);
         }
       }
-      const int page0 = off + s0;   // first page of the segment within the unit
-      // page id of segment page i; -1 past the segment's end
-      auto pid_of = [&](int i) { return i < seg ? __builtin_amdgcn_readlane(pidv, min(i, 63)) : -1; };
-      // Scores segment page i from pf; a step past the segment's end (live
-      // false) computes on page 0's data and stores nothing.
-      auto score_page = [&](int i, const PageFrags& pf) {
-        const bool live = i < seg;
-        const int32_t pid = pid_of(i);
-        const bool ok = pid >= 0 && pid < a.num_pages;
-        // all four fragments are scored before any store, so their MFMAs and
-        // epilogues share one scheduling region
-        float v[kFragsPerPage];
+      // scored keys of this unit: whole 16-key fragments up to the longest row
+      covered = min(a.width, (t.lmax + 15) / 16 * 16);
+      row_ok = my_q < t.nq;
+      // selects instead of an indexed read, which would put the array in LDS
+      my_len = (my_q & 2) ? ((my_q & 1) ? t.len[3] : t.len[2]) : ((my_q & 1) ? t.len[1] : t.len[0]);
+      out_row = a.logits + (int64_t)(row_ok ? t.r_base + my_q : 0) * a.ld;
+    }
+    claim();   // the next chunk's page ids load while this chunk is scored
+
+    // Scores chunk page i from pf; a step past the chunk's end (live false)
+    // computes on page 0's data and stores nothing.
+    auto score_page = [&](int i, const PageFrags& pf) {
+      const bool live = i < cur_n;
+      const int32_t pid = __builtin_amdgcn_readlane(cur_pidv, i);
+      const bool ok = pid >= 0 && pid < a.num_pages;
+      // all four fragments are scored before any store, so their MFMAs and
+      // epilogues share one scheduling region
+      float v[kFragsPerPage];
 #pragma unroll
-        for (int f = 0; f < kFragsPerPage; ++f)
-          v[f] = fragment_logit(qf, pf.b[f]) * __shfl(pf.sc, f * 16 + (lane & 15));
+      for (int f = 0; f < kFragsPerPage; ++f)
+        v[f] = fragment_logit(qf, pf.b[f]) * __shfl(pf.sc, f * 16 + (lane & 15));
 #pragma unroll
-        for (int f = 0; f < kFragsPerPage; ++f) {
-          const int j = (page0 + i) * kPage + f * 16 + (lane & 15);
-          const bool val = ok && j < my_len;
-          if (live && row_ok && j < covered && (val || clean)) out_row[j] = val ? v[f] : -INFINITY;
-        }
-      };
-      // DEPTH - 1 pages are loading while one is scored; the loop runs whole
-      // groups of DEPTH steps, the steps past the segment's end storing nothing.
-      PageFrags buf[DEPTH];
-#pragma unroll
-      for (int d = 0; d < DEPTH - 1; ++d) load_page(a, pid_of(d), lane, buf[d]);
-      for (int i = 0; i < seg; i += DEPTH) {
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-          load_page(a, pid_of(i + d + DEPTH - 1), lane, buf[(d + DEPTH - 1) % DEPTH]);
-          score_page(i + d, buf[d]);
-        }
+      for (int f = 0; f < kFragsPerPage; ++f) {
+        const int j = (cur_pg + i) * kPage + f * 16 + (lane & 15);
+        const bool val = ok && j < my_len;
+        if (live && row_ok && j < covered && (val || clean)) out_row[j] = val ? v[f] : -INFINITY;
       }
+    };
+    // One page loads while the previous one is scored; the chunk's last step
+    // loads the next chunk's first page.
+#pragma unroll
+    for (int d = 0; d < kChunk; ++d) {
+      int32_t np;
+      if (d + 1 < kChunk)
+        np = d + 1 < cur_n ? __builtin_amdgcn_readlane(cur_pidv, d + 1) : -1;
+      else
+        np = nx_n > 0 ? __builtin_amdgcn_readfirstlane(nx_ids) : -1;
+      load_page(a, np, lane, buf[(d + 1) % DEPTH]);
+      score_page(d, buf[d % DEPTH]);
     }
   }
 
@@ -204,18 +252,18 @@ __global__ __launch_bounds__(64 * kPagedWaves, 2) void logits_paged_kernel(Paged
   int64_t f0 = 0, fn = 0;
   split_range((int64_t)units * blocks, waves_total, gw, f0, fn);
   int cur = -1;
-  Unit t{};
-  int covered = 0;
+  Unit ft{};
+  int fcovered = 0;
   for (int64_t x = f0; x < f0 + fn; ++x) {
     const int fu = (int)(x / blocks);
     const int j = (int)(x - (int64_t)fu * blocks) * kPage + lane;
     if (fu != cur) {
       cur = fu;
-      t = unit_at(a, qgroups, fu);
-      covered = min(a.width, (t.lmax + 15) / 16 * 16);
+      ft = unit_at(a, qgroups, fu);
+      fcovered = min(a.width, (ft.lmax + 15) / 16 * 16);
     }
-    if (j >= covered && j < a.width) {
-      for (int qi = 0; qi < t.nq; ++qi) a.logits[(int64_t)(t.r_base + qi) * a.ld + j] = -INFINITY;
+    if (j >= fcovered && j < a.width) {
+      for (int qi = 0; qi < ft.nq; ++qi) a.logits[(int64_t)(ft.r_base + qi) * a.ld + j] = -INFINITY;
     }
   }
 }
