@@ -614,7 +614,26 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
   bool done = false;
   bool row_written = false;   // output row including padding already stored
   if (kk > 0u && C >= kk && C <= (uint32_t)CAP) {
-    if (sampled) {
+    bool binned = sampled;
+    if (!sampled && C > kk) {
+      // An unsampled list (every key of a short segment, or a merge level's candidates) is binned
+      // between its own smallest and largest code, as a sampled list is between T and the sample
+      // maximum: one histogram pass instead of a radix select.
+      uint32_t cmin = 0xffffffffu, cmax = 0u, unused = 0u;
+      for (uint32_t i = tid; i < C; i += THREADS) {
+        cmin = min(cmin, sh.cand[i].x);
+        cmax = max(cmax, sh.cand[i].x);
+      }
+      block_min_max_sum<NW>(cmin, cmax, unused, sh.w0, sh.w1, sh.w2);
+      T = cmin;   // >= 1: every listed code is
+      const uint32_t range = cmax - cmin;
+      bshift = range >> kDigitBits ? (uint32_t)(32 - __builtin_clz(range) - kDigitBits) : 0u;
+#pragma unroll
+      for (int i = 0; i < kBins / THREADS; ++i) sh.hist[tid * (kBins / THREADS) + i] = 0u;
+      __syncthreads();
+      binned = true;
+    }
+    if (binned) {
       // ---- 3. the bin of the k-th candidate ------------------------------------
       // Each thread handles list entries tid + THREADS * j in chunks of kRegPairs
       // held in registers (one chunk, read once, when the list is small).
