@@ -701,15 +701,38 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
               stage[bitmap_rank(sh.bits, sh.hist, pos)] = reg[j];
           }
           __syncthreads();
-          for (int o = tid; o < a.k; o += THREADS) {
-            if (o < (int)kk) {
-              const v2u e = stage[o];
-              emit((uint32_t)o, e.y, e.x);
-            } else if (FINAL) {
-              a.out[out_base + o] = -1;
-            } else {
-              a.out_keys[out_base + o] = 0u;
-              a.out_idx[out_base + o] = -1;
+          // A thread's outputs in batches: every source-index load of a batch, then every map
+          // load, then the stores, so the loads of a batch are in flight together.
+          constexpr int kOutBatch = 8;
+          for (int o0 = 0; o0 < a.k; o0 += THREADS * kOutBatch) {
+            int32_t jv[kOutBatch];
+            uint32_t cv[kOutBatch];
+#pragma unroll
+            for (int b = 0; b < kOutBatch; ++b) {
+              const int o = o0 + b * THREADS + tid;
+              const v2u e = o < (int)kk ? stage[o] : v2u{0u, 0u};
+              cv[b] = e.x;
+              jv[b] = -1;
+              if (o < (int)kk) jv[b] = LEVEL0 ? (int32_t)(lb + e.y) : a.in_idx[(int64_t)row * a.in_len + lb + e.y];
+            }
+            if (FINAL) {
+#pragma unroll
+              for (int b = 0; b < kOutBatch; ++b) {
+                const int o = o0 + b * THREADS + tid;
+                jv[b] = o < (int)kk ? map_index(map, req, row_ks, jv[b]) : -1;
+              }
+            }
+#pragma unroll
+            for (int b = 0; b < kOutBatch; ++b) {
+              const int o = o0 + b * THREADS + tid;
+              if (o < a.k) {
+                if (FINAL) {
+                  a.out[out_base + o] = jv[b];
+                } else {
+                  a.out_keys[out_base + o] = o < (int)kk ? cv[b] : 0u;
+                  a.out_idx[out_base + o] = jv[b];
+                }
+              }
             }
           }
           row_written = true;
