@@ -7,7 +7,7 @@ import torch
 import fp8_mqa_logits_amd as F
 from oracle import mqa_logits, paged_mqa_logits
 from tests.parity import assert_logits_close, cancellation_tol, to_dev
-from workloads.generate import H, D, ragged_inputs, multi_request_ragged, paged_inputs
+from workloads.generate import H, D, config_inputs, ragged_inputs, multi_request_ragged, paged_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -92,6 +92,26 @@ def test_ragged_repeats_streams_and_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(static_out, ref_a), f"graph replay {rep}"
         assert torch.equal(eager, ref_b), f"eager launch after replay {rep}"
+
+
+@pytest.mark.parametrize("name", ["prefill_64k", "prefill_35k"])
+def test_full_size_ragged_logits_sampled_rows(name):
+    """One launch at the full prefill shape (every workgroup resident, work handed out by the device
+    queues, queues stealing from each other at the end): sampled rows of its output, element by element,
+    against the oracle, with clean set so the -inf outside each window is checked too."""
+    inp = config_inputs(name)
+    d = _ragged_dev(inp)
+    g = F.indexer_logits_ragged(*d, clean=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    # first and last rows, both rows of every 16-row block edge sampled, and random rows
+    rows = sorted({0, 1, 15, 16, 4095, 4096, inp.m - 17, inp.m - 16, inp.m - 1} |
+                  set(rng.integers(0, inp.m, 5).tolist()))
+    ridx = np.array(rows)
+    got = g[torch.as_tensor(ridx, device=g.device)].cpu().numpy()
+    del g
+    o = mqa_logits(inp.q[ridx], inp.kv, inp.kv_scale, inp.weights[ridx], inp.ks[ridx], inp.ke[ridx])
+    assert_logits_close(got, o, inp.ks[ridx], inp.ke[ridx], clean=True, what=f"{name} full launch")
 
 
 @pytest.mark.parametrize("m,n", [(1, 17), (5, 64), (16, 65), (37, 1000), (50, 3000), (33, 4133)])
