@@ -15,19 +15,20 @@
 //   accumulation registers) with its online-softmax state.  One wave per SIMD
 //   leaves each wave the whole register file.  The splits merge in a second
 //   kernel.
-// - Keys stream through LDS in 64-key steps, double buffered, as fp8: once
-//   row-major (576 bytes per key, for the scores) and once transposed (keys
-//   contiguous per latent dimension, for the value product).  Each thread
-//   gathers two 16-byte latent chunks of 4 keys and one rotary chunk, and
-//   transposes its 4 x 4 byte tiles with byte permutes while storing, so no
-//   extra LDS pass is needed.  The split's slot ids are read into LDS once, so
-//   a gather never waits on an id load; the gather of step i + 2 is in flight
-//   while step i is computed.
+// - Keys stream through LDS in 64-key steps, double buffered, as fp8 rows
+//   (576 bytes per key, 8 bytes of bank skew).  Each thread gathers two
+//   16-byte latent chunks of 4 keys and one rotary chunk.  The split's slot ids
+//   are read into LDS once, so a gather never waits on an id load; the gather
+//   of step i + 2 is in flight while step i is computed.
 // - Scores are computed transposed, S^T = K Q^T (16x16x32 bf16 MFMA, fp8
 //   widened to bf16 exactly at operand load): a lane then holds 4 consecutive
 //   keys of one head, which is exactly the A-operand layout of P in P V, so
-//   the probabilities never leave registers.  The value operand reads 4 + 4
-//   transposed fp8 bytes per lane.
+//   the probabilities never leave registers.  The value operand comes from the
+//   same row-major tile through the LDS transpose read (ds_read_b64_tr_b8):
+//   within 16 lanes, lane i < 8 receives byte i of the 8-byte rows that the
+//   even lanes address and lane 8 + i byte i of the odd lanes' rows, so lanes
+//   2t and 2t + 1 pointing at key t's row (columns c .. c + 7 and c + 8 ..
+//   c + 15) hand lane n column c + n of the 8 keys.
 // - Softmax works in log2 units; the running maximum is raised (and the
 //   output rescaled) only when a step's maximum exceeds it by more than 8,
 //   which keeps every weight below 2^8 and skips most rescales.
@@ -45,9 +46,7 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 constexpr int kMlaThreads = 256;
 constexpr int kMlaHeadsPerWg = 64;
 constexpr int kKRow = kMlaDqk + 8;            // LDS bytes per key, row-major (8 bytes of bank skew)
-constexpr int kVtRow = kMlaBlock + 4;         // LDS bytes per latent dimension, transposed
 constexpr int kKBytes = kMlaBlock * kKRow;    // 37376
-constexpr int kVtBytes = kMlaDv * kVtRow;     // 34816
 constexpr int kKSteps = kMlaDqk / 32;         // 18 score k-steps of 32 values
 constexpr int kVTiles = kMlaDv / 16;          // 32 output tiles of 16 values
 constexpr float kLog2e = 1.4426950408889634f;
@@ -57,7 +56,6 @@ constexpr int kMlaMaxSplitKeys = 2048;        // slot ids of one split held in L
 
 struct MlaStage {
   uint8_t k[2][kKBytes];
-  uint8_t vt[2][kVtBytes];
   float mul[2][kMlaBlock];   // sm_scale * log2(e) * kv_scale; NaN marks a masked key
   float vsc[2][kMlaBlock];   // kv_scale; 0 for a masked key
   int32_t idx[kMlaMaxSplitKeys];   // the split's slot ids (-1 past its end)
@@ -81,18 +79,6 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 
 __device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// 4 x 4 byte transpose: y[i] byte q = x[q] byte i.
-__device__ __forceinline__ void transpose4x4(const uint32_t (&x)[4], uint32_t (&y)[4]) {
-  const uint32_t t0 = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);
-  const uint32_t t1 = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);
-  const uint32_t t2 = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
-  const uint32_t t3 = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
-  y[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
-  y[1] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
-  y[2] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
-  y[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
 __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArgs a, int nsplit,
@@ -157,7 +143,6 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
   };
   auto stage_store = [&](int buf, const MlaGather& st) {
     uint8_t* K = sh.k[buf];
-    uint8_t* Vt = sh.vt[buf];
     // rows are 8-byte aligned (584-byte stride), so 16-byte chunks go out as two 8-byte stores
     auto put16 = [](uint8_t* dst, const v4i& v) {
       reinterpret_cast<uint2*>(dst)[0] = uint2{(uint32_t)v[0], (uint32_t)v[1]};
@@ -169,20 +154,6 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
       put16(K + (4 * sq + q4) * kKRow + 16 * (sc + 16), st.lat[q4][1]);
     }
     put16(K + rk * kKRow + 16 * rc, st.rot);
-#pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
-      const int chunk = sc + 16 * ch;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x[4] = {(uint32_t)st.lat[0][ch][w], (uint32_t)st.lat[1][ch][w], (uint32_t)st.lat[2][ch][w],
-                               (uint32_t)st.lat[3][ch][w]};
-        uint32_t y[4];
-        transpose4x4(x, y);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<uint32_t*>(Vt + (16 * chunk + 4 * w + i) * kVtRow + 4 * sq) = y[i];
-      }
-    }
     if (tid < kMlaBlock) {
       sh.mul[buf][tid] = st.ok ? a.sm_scale * kLog2e * st.scale : __builtin_nanf("");
       sh.vsc[buf][tid] = st.ok ? st.scale : 0.f;
@@ -206,7 +177,6 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
   // One step of scores, softmax and value product on LDS buffer cb.
   auto compute = [&](int cb) {
     const uint8_t* K = sh.k[cb];
-    const uint8_t* Vt = sh.vt[cb];
 
     // scores S^T: tile kt rows = keys 16 kt + 4 g + r, column = head l16
     v4f S[4];
@@ -267,15 +237,19 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
       }
       lrun += ps;
     }
-    // O += P V: value tile n, lane column 16 n + l16
+    // O += P V: value tile n, lane column 16 n + l16.  The B operand of key step ks2 holds keys
+    // 32 ks2 + 4 g .. +4 and 32 ks2 + 16 + 4 g .. +4 (the order of P's elements); lane pair
+    // (2 t, 2 t + 1) of each 16 points at the t-th of those keys' row, columns 16 n and 16 n + 8.
+    const int tkey = (l16 >> 1) < 4 ? 4 * g + (l16 >> 1) : 16 + 4 * g + (l16 >> 1) - 4;
+    const uint8_t* vrow = K + tkey * kKRow + 8 * (l16 & 1);
 #pragma unroll
     for (int n = 0; n < kVTiles; ++n) {
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const uint8_t* vp = Vt + (16 * n + l16) * kVtRow + 32 * ks2 + 4 * g;
-        const uint32_t w0 = *reinterpret_cast<const uint32_t*>(vp);
-        const uint32_t w1 = *reinterpret_cast<const uint32_t*>(vp + 16);
-        O[n] = mfma_bf16(P[ks2], fp8x8_to_bf16(w0, w1), O[n]);
+        typedef int v2i_t __attribute__((ext_vector_type(2)));
+        const v2i_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i_t*)(vrow + 32 * ks2 * kKRow + 16 * n));
+        O[n] = mfma_bf16(P[ks2], fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]), O[n]);
       }
     }
 
