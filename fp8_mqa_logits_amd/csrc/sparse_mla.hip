@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
   if (nblk > 1) stage_load(1, ga);
   __syncthreads();
   for (int blk = 0; blk < nblk; ++blk) {
-    compute(blk & 1);
+    if (head_ok) compute(blk & 1);   // a wave past the last head only helps stage the keys
     if (blk + 1 < nblk) stage_store((blk + 1) & 1, ga);
     if (blk + 2 < nblk) stage_load(blk + 2, ga);
     __syncthreads();
