@@ -31,7 +31,9 @@
 //   c + 15) hand lane n column c + n of the 8 keys.
 // - Softmax works in log2 units; the running maximum is raised (and the
 //   output rescaled) only when a step's maximum exceeds it by more than 8,
-//   which keeps every weight below 2^8 and skips most rescales.
+//   which keeps every weight below 2^8 and skips most rescales.  Powers of 2
+//   use the hardware exp2 directly: weights below 2^-126 flush to 0, which
+//   is far below what the bf16 probabilities can carry.
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
     const bool need = bm > mrun + kLazy || (mrun == -INFINITY && bm > -INFINITY);
     if (ballot64(need) != 0ull) {
       const float mnew = need ? bm : mrun;
-      const float alpha = mnew == mrun ? 1.f : exp2f(mrun - mnew);
+      const float alpha = mnew == mrun ? 1.f : __builtin_amdgcn_exp2f(mrun - mnew);
       lrun *= alpha;
       mrun = mnew;
 #pragma unroll
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
         const v4f vsc = *reinterpret_cast<const v4f*>(&sh.vsc[cb][16 * kt + 4 * g]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float pr = mrun == -INFINITY ? 0.f : exp2f(S[kt][r] - mrun);
+          const float pr = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(S[kt][r] - mrun);
           ps += pr;
           P[kt >> 1][4 * (kt & 1) + r] = (__bf16)(pr * vsc[r]);
         }
