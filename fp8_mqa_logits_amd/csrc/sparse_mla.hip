@@ -47,9 +47,9 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 constexpr int kMlaThreads = 256;
 constexpr int kMlaHeadsPerWg = 64;
-constexpr int kKRow = kMlaDqk + 8;            // LDS bytes per key, row-major (8 bytes of bank skew)
-constexpr int kKBytes = kMlaBlock * kKRow;    // 37376
-constexpr int kKSteps = kMlaDqk / 32;         // 18 score k-steps of 32 values
+constexpr int kKRow = kMlaDqk + 16;           // LDS bytes per key, row-major (16 bytes of bank skew)
+constexpr int kKBytes = kMlaBlock * kKRow;    // 37888
+constexpr int kLatChunks = kMlaDv / 128;      // 4 fp8 score chunks of 128 latent values
 constexpr int kVTiles = kMlaDv / 16;          // 32 output tiles of 16 values
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -101,17 +101,67 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
   const int nblk = k_end > k_begin ? (k_end - k_begin + kMlaBlock - 1) / kMlaBlock : 0;
   const int32_t* __restrict__ idx_row = a.indices + (int64_t)t * a.ld_idx;
 
-  // ---- q of this wave's head tile: B operand of S^T (lane: head l16, values 32 ks + 8 g .. +8)
+  // ---- q of this wave's head tile, the B operand of S^T.
+  // The 512 latent values go to the fp8 MFMA as two e4m3fn parts with a power-of-2 scale per
+  // hardware k-block of 32: q 2^e = hi + lo, the block maximum scaled into [128, 256).  hi holds 4
+  // significant bits and lo the rest of bf16's 8, so the split is exact for every value above
+  // 2^-10 times its block maximum (smaller ones fall under e4m3's subnormal grid and lose bits).
+  // In the 16x16x128 fp8 operand, bytes 0-15 of lane group g feed k-block g/2 and bytes 16-31 feed
+  // k-block 2 + g/2, and k-block G takes its scale from lane group G: so a block is the same half
+  // of lanes l and l ^ 16, and its exponent is moved to lane group G by a shuffle.  The 64 rotary
+  // values stay bf16 (two k-steps of 32 values).
   const int head0 = hb * kMlaHeadsPerWg + ht * 16;   // first head of the tile (H is a multiple of 16)
   const bool head_ok = head0 < a.H;
-  v8bf qf[kKSteps];
+  v8i qh[kLatChunks], ql[kLatChunks];
+  int qsc[kLatChunks];   // E8M0 code of 2^-e of k-block g of chunk c
+  v8bf qr[2];
   {
     const uint16_t* qrow = a.q + ((int64_t)t * a.H + (head_ok ? head0 + l16 : 0)) * kMlaDqk;
+    const int src = l16 + 32 * (g & 1);   // a lane of the first pair holding k-block g
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
+    for (int c = 0; c < kLatChunks; ++c) {
+      float x[32];
+      float amax[2] = {0.f, 0.f};   // of bytes 0-15 and 16-31
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        v4i raw = {0, 0, 0, 0};
+        if (head_ok) raw = *reinterpret_cast<const v4i*>(qrow + 128 * c + 32 * g + 8 * v);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          x[8 * v + 2 * w] = __uint_as_float((uint32_t)raw[w] << 16);
+          x[8 * v + 2 * w + 1] = __uint_as_float((uint32_t)raw[w] & 0xffff0000u);
+          amax[v >> 1] = fmaxf(amax[v >> 1], fmaxf(fabsf(x[8 * v + 2 * w]), fabsf(x[8 * v + 2 * w + 1])));
+        }
+      }
+      int e[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int ex = 0;
+        frexpf(fmaxf(amax[h], __shfl_xor(amax[h], 16)), &ex);   // max = m 2^ex, m in [0.5, 1)
+        e[h] = min(max(8 - ex, -127), 127);
+      }
+      const int e_lo = __shfl(e[0], src), e_hi = __shfl(e[1], src);
+      qsc[c] = 127 - (g < 2 ? e_lo : e_hi);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ei = e[i >> 2];
+        const float y0 = ldexpf(x[4 * i], ei), y1 = ldexpf(x[4 * i + 1], ei);
+        const float y2 = ldexpf(x[4 * i + 2], ei), y3 = ldexpf(x[4 * i + 3], ei);
+        int hw = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+        hw = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, hw, true);
+        const auto d0 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);   // the hi values, exactly
+        const auto d1 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+        int lw = __builtin_amdgcn_cvt_pk_fp8_f32(y0 - d0[0], y1 - d0[1], 0, false);
+        lw = __builtin_amdgcn_cvt_pk_fp8_f32(y2 - d1[0], y3 - d1[1], lw, true);
+        qh[c][i] = hw;
+        ql[c][i] = lw;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
       v4i raw = {0, 0, 0, 0};
-      if (head_ok) raw = *reinterpret_cast<const v4i*>(qrow + 32 * ks + 8 * g);
-      qf[ks] = __builtin_bit_cast(v8bf, raw);
+      if (head_ok) raw = *reinterpret_cast<const v4i*>(qrow + kMlaDv + 32 * j + 8 * g);
+      qr[j] = __builtin_bit_cast(v8bf, raw);
     }
   }
 
@@ -145,11 +195,7 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
   };
   auto stage_store = [&](int buf, const MlaGather& st) {
     uint8_t* K = sh.k[buf];
-    // rows are 8-byte aligned (584-byte stride), so 16-byte chunks go out as two 8-byte stores
-    auto put16 = [](uint8_t* dst, const v4i& v) {
-      reinterpret_cast<uint2*>(dst)[0] = uint2{(uint32_t)v[0], (uint32_t)v[1]};
-      reinterpret_cast<uint2*>(dst)[1] = uint2{(uint32_t)v[2], (uint32_t)v[3]};
-    };
+    auto put16 = [](uint8_t* dst, const v4i& v) { *reinterpret_cast<v4i*>(dst) = v; };
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       put16(K + (4 * sq + q4) * kKRow + 16 * sc, st.lat[q4][0]);
@@ -180,17 +226,30 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
   auto compute = [&](int cb) {
     const uint8_t* K = sh.k[cb];
 
-    // scores S^T: tile kt rows = keys 16 kt + 4 g + r, column = head l16
+    // scores S^T: tile kt rows = keys 16 kt + 4 g + r, column = head l16.  Latent chunk c: the key
+    // codes straight from LDS (lane: key 16 kt + l16, bytes 128 c + 32 g .. +32) against q's hi and
+    // lo parts, scaled by 2^-e; rotary: bf16 MFMAs on the widened codes.
     v4f S[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) S[kt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
+    for (int c = 0; c < kLatChunks; ++c) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const uint8_t* p = K + (16 * kt + l16) * kKRow + 32 * ks + 8 * g;
+        const v4i* p = reinterpret_cast<const v4i*>(K + (16 * kt + l16) * kKRow + 128 * c + 32 * g);
+        const v4i w0 = p[0], w1 = p[1];
+        const v8i kf = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+        S[kt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qh[c], S[kt], 0, 0, 0, 127, 0, qsc[c]);
+        S[kt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, ql[c], S[kt], 0, 0, 0, 127, 0, qsc[c]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const uint8_t* p = K + (16 * kt + l16) * kKRow + kMlaDv + 32 * j + 8 * g;
         const uint2 w = *reinterpret_cast<const uint2*>(p);
-        S[kt] = mfma_bf16(fp8x8_to_bf16(w.x, w.y), qf[ks], S[kt]);
+        S[kt] = mfma_bf16(fp8x8_to_bf16(w.x, w.y), qr[j], S[kt]);
       }
     }
 
