@@ -55,6 +55,7 @@ def _args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_64k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the on-box MFMA and copy peak probes")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--fused-check", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -210,16 +211,79 @@ class PagedStep:
 
 
 def _time_steps(step, steps, warmup, record):
+    """Wall ms per step over `steps` timed steps; with record, per-launch and per-step HIP events
+    (on the launch stream) are kept on the step for the kernel times and the step distribution."""
     import torch
     for _ in range(warmup):
         step.run()
     torch.cuda.synchronize()
     step.events = []
+    step.step_events = []
     t0 = time.perf_counter()
     for _ in range(steps):
+        if record:
+            se = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            se[0].record()
         step.run(record=record)
+        if record:
+            se[1].record()
+            step.step_events.append(se)
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def _distribution(step):
+    """Median and min of the step and per-launch kernel times (ms) of the last timed run."""
+    st = [e[0].elapsed_time(e[1]) for e in step.step_events]
+    lt = [ev[0].elapsed_time(ev[1]) for ev, _ in step.events]
+    tt = [ev[1].elapsed_time(ev[2]) for ev, _ in step.events]
+    return {"step_ms_median": round(_median(st), 4), "step_ms_min": round(min(st), 4),
+            "logits_launch_ms_median": round(_median(lt), 4), "logits_launch_ms_min": round(min(lt), 4),
+            "topk_launch_ms_median": round(_median(tt), 4), "topk_launch_ms_min": round(min(tt), 4)}
+
+
+def measured_peaks():
+    """On-box peaks next to the published ones.
+
+    mfma: the library's fp8 MFMA throughput probe (2 workgroups of 256 threads per CU, each wave
+    4 x 4096 back-to-back 16x16x128 fp8 MFMAs on four accumulators), HIP events around 5 launches.
+    copy: a device-to-device copy of 1 GiB (torch copy_), read plus written bytes, 5 copies.
+    """
+    import torch
+    import fp8_mqa_logits_amd as F
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters, reps = 2 * cus, 4096, 5
+    out, flops = F.fp8idx_probe_mfma_fp8(blocks, iters)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        F.fp8idx_probe_mfma_fp8(blocks, iters, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    mfma_tflops = flops / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
+    nbytes = 1 << 30
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2.0 * nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    del x, y, out
+    torch.cuda.empty_cache()
+    return {"mfma_fp8_tflops": round(mfma_tflops, 1), "copy_gbps": round(copy_gbps, 1),
+            "mfma_probe": f"{blocks} x 256 threads, 4 x {iters} fp8 16x16x128 MFMAs per wave, {reps} launches",
+            "copy_probe": f"1 GiB device copy, read + written bytes, {reps} copies"}
 
 
 def _time_fused(step, steps, warmup, overlap=False):
@@ -596,8 +660,16 @@ def main():
         out["config"].update({"m": inp.m, "n": inp.n, "H": H, "D": D, "k": inp.k,
                               "logits_cap_bytes": inp.cap_bytes, "rows_per_chunk": step.rpc,
                               "valid_pairs": inp.valid_pairs})
+    out.update(_distribution(step))
     if "fused_ms_per_step" in r:
         out["fused_ms_per_step"] = round(r["fused_ms_per_step"], 4)
+    if not a.no_peaks:
+        pk = measured_peaks()
+        if paged:
+            pk["logits_frac_of_copy"] = round(roof["achieved"] / pk["copy_gbps"], 4)
+        else:
+            pk["logits_frac_of_mfma_probe"] = round(roof["achieved"] / pk["mfma_fp8_tflops"], 4)
+        out["measured_peaks"] = pk
     if not a.no_cpu_baseline and not paged:
         out["cpu_baseline"] = _cpu_baseline(inp, a.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -33,4 +33,5 @@ from .binding import (  # noqa: F401
     fp8idx_workspace_bytes_paged,
     fp8idx_rows_per_chunk,
     fp8idx_version,
+    fp8idx_probe_mfma_fp8,
 )

@@ -35,7 +35,7 @@ EXPORTED = (
     "fp8idx_status_string", "fp8idx_last_hip_error", "fp8idx_version",
     "indexer_quant_fp8", "indexer_logits_topk_ragged_overlap",
     "indexer_prepare_ragged", "indexer_prepare_decode",
-    "indexer_sparse_mla", "fp8idx_sparse_mla_workspace_bytes",
+    "indexer_sparse_mla", "fp8idx_sparse_mla_workspace_bytes", "fp8idx_probe_mfma_fp8",
 )
 
 MLA_DQK = 576   # sparse MLA KV row: 512 latent + 64 rotary values
@@ -102,6 +102,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "indexer_sparse_mla": (_I32, [_P, _P, _P, _I64, _P, _I64, _I32, _I32, _I32, _I32, _I32, ctypes.c_float,
                                       _P, _P, _P, _SZ, _P]),
         "fp8idx_sparse_mla_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+        "fp8idx_probe_mfma_fp8": (_I32, [_I32, _I32, _P, ctypes.POINTER(ctypes.c_double), _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -396,6 +397,27 @@ def indexer_logits_topk_paged(q, kv_pool, scale_pool, weights, row_len, block_ta
             int(bool(map_to_slots)), _ptr(out), out.shape[1], logits_cap_bytes, wp, wb, _stream(dev, stream))
     _check("indexer_logits_topk_paged", st)
     return out
+
+
+def fp8idx_probe_mfma_fp8(blocks: int, iters: int, *, out: Optional[torch.Tensor] = None, stream=None):
+    """Launch the fp8 MFMA throughput probe (a measurement helper, not an indexer step).
+
+    Returns (out, flops): out is the float32 [blocks * 256] sink the kernel writes, flops the
+    launch's MFMA flops.  The caller times the launch (events on `stream`).
+    """
+    dev = torch.device("cuda", torch.cuda.current_device())
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", _F32, dev)
+        if out.numel() < blocks * 256:
+            raise ValueError("out must hold blocks * 256 floats")
+    flops = ctypes.c_double(0.0)
+    L = load_library()
+    with torch.cuda.device(dev):
+        st = L.fp8idx_probe_mfma_fp8(int(blocks), int(iters), _ptr(out), ctypes.byref(flops), _stream(dev, stream))
+    _check("fp8idx_probe_mfma_fp8", st)
+    return out, flops.value
 
 
 def indexer_quant_fp8(x, *, codes: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,

@@ -280,6 +280,15 @@ fp8idx_status indexer_prepare_decode(const int32_t* seq_len, const int32_t* req_
   return e == hipSuccess ? FP8IDX_OK : hip_fail(e);
 }
 
+fp8idx_status fp8idx_probe_mfma_fp8(int32_t blocks, int32_t iters, float* out, double* flops, void* stream) {
+  if (blocks <= 0 || iters <= 0 || !out || !aligned(out, 4)) return FP8IDX_EINVAL;
+  DeviceInfo dev;
+  if (fp8idx_status s = current_device(&dev)) return s;
+  if (flops) *flops = (double)blocks * (fp8idx::kProbeThreads / 64) * (double)iters * fp8idx::kProbeChains * 65536.0;
+  const hipError_t e = fp8idx::launch_mfma_probe(blocks, iters, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8IDX_OK : hip_fail(e);
+}
+
 fp8idx_status indexer_quant_fp8(const float* x, int64_t ld_x, int64_t rows, int32_t D, uint8_t* codes,
                                 int64_t ld_codes, float* scale, void* stream) {
   if (D < 4 || D > 2048 || D % 4 != 0) return FP8IDX_EUNSUPPORTED;

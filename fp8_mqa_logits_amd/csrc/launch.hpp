@@ -169,4 +169,10 @@ struct SparseMlaPlan {
 SparseMlaPlan plan_sparse_mla(int32_t T, int32_t H, int32_t topk);
 hipError_t launch_sparse_mla(const SparseMlaArgs& a, const SparseMlaPlan& plan, void* ws, hipStream_t s);
 
+// fp8 MFMA throughput probe: blocks x kProbeThreads threads, each wave iters x kProbeChains MFMAs;
+// one float per thread to out (keeps the work live).
+constexpr int kProbeChains = 4;
+constexpr int kProbeThreads = 256;
+hipError_t launch_mfma_probe(int blocks, int iters, float* out, hipStream_t s);
+
 }  // namespace fp8idx

@@ -1,0 +1,46 @@
+// Sustained fp8 MFMA throughput on this device, for the roofline report.  Not a
+// step of the indexer: it gives the measured peak that the logits kernel's
+// MFMA rate is set against, next to the published 5.0 PFLOP/s dense fp8 figure.
+//
+// Each wave issues back-to-back v_mfma_f32_16x16x128_f8f6f4 on kProbeChains
+// independent accumulators (enough to cover the MFMA result latency), with
+// operands held in registers, so nothing but the matrix pipe and the issue
+// slot is exercised.  One MFMA is 2 * 16 * 16 * 128 = 65536 flops.
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+#include <fp8idx.h>
+
+namespace fp8idx {
+
+__global__ __launch_bounds__(kProbeThreads) void mfma_probe_kernel(int iters, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  // e4m3fn codes 0x30..0x37 (0.5 .. 0.9375): finite, so sums stay finite
+  const int bytes = 0x30 + (lane & 7);
+  const int word = bytes * 0x01010101;
+  v8i a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = word;
+    b[i] = word ^ (i << 24);
+  }
+  v4f acc[kProbeChains];
+#pragma unroll
+  for (int j = 0; j < kProbeChains; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < kProbeChains; ++j) acc[j] = mfma_fp8_16x16x128(a, b, acc[j]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kProbeChains; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+  out[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;
+}
+
+hipError_t launch_mfma_probe(int blocks, int iters, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), 0, s, iters, out);
+  return hipGetLastError();
+}
+
+}  // namespace fp8idx

@@ -366,6 +366,21 @@ FP8IDX_API size_t fp8idx_workspace_bytes_paged(int32_t B, int32_t next_n, int32_
  * stride of the workspace logits); cap 0 gives rows.  Pure host arithmetic. */
 FP8IDX_API int32_t fp8idx_rows_per_chunk(size_t logits_cap_bytes, int64_t width, int32_t rows);
 
+/*
+ * Measurement helper, not a step of the indexer: a sustained fp8 MFMA
+ * throughput probe, the measured peak that the logits kernel's MFMA rate is
+ * reported against next to the published dense fp8 figure.  Launches
+ * `blocks` workgroups of 256 threads; each wave issues iters x 4
+ * back-to-back v_mfma_f32_16x16x128_f8f6f4 on four independent accumulators
+ * with register operands.  out: device float32 [blocks * 256], written (one
+ * value per thread, which keeps the work live; its value means nothing).
+ * *flops (if non-NULL) receives the flops of the launch:
+ * blocks * 4 waves * iters * 4 * 65536.  blocks > 0 and iters > 0, else
+ * FP8IDX_EINVAL.  Allocates nothing; runs on `stream`; the caller times it.
+ */
+FP8IDX_API fp8idx_status fp8idx_probe_mfma_fp8(int32_t blocks, int32_t iters, float* out, double* flops,
+                                               void* stream);
+
 /* Static string naming a status. */
 FP8IDX_API const char* fp8idx_status_string(int32_t status);
 

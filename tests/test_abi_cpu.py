@@ -34,7 +34,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.EXPORTED) == names
@@ -260,3 +260,12 @@ def test_sparse_mla_validation(lib):
     assert call(T=2, topk=2048, ld=2048, ws=P + 16, wsb=need) == EINVAL   # 256-byte alignment
     assert call(T=2, topk=2048, ld=2048, ws=P, wsb=need) == EDEV
     assert lib.fp8idx_sparse_mla_workspace_bytes(256, 64, 2048) == 0     # one workgroup per token already
+
+
+def test_mfma_probe_validation(lib):
+    flops = ctypes.c_double(0.0)
+    assert lib.fp8idx_probe_mfma_fp8(0, 8, P, ctypes.byref(flops), NULL) == EINVAL
+    assert lib.fp8idx_probe_mfma_fp8(4, 0, P, ctypes.byref(flops), NULL) == EINVAL
+    assert lib.fp8idx_probe_mfma_fp8(4, 8, NULL, ctypes.byref(flops), NULL) == EINVAL
+    assert lib.fp8idx_probe_mfma_fp8(4, 8, P + 2, ctypes.byref(flops), NULL) == EINVAL
+    assert lib.fp8idx_probe_mfma_fp8(4, 8, P, ctypes.byref(flops), NULL) == EDEV
