@@ -56,6 +56,8 @@ def _args():
     ap.add_argument("--workload", default="prefill_64k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the on-box MFMA and copy peak probes")
+    ap.add_argument("--cold", action="store_true",
+                    help="rewrite a 512 MiB scratch buffer before each timed step (cold caches)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--fused-check", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -210,17 +212,24 @@ class PagedStep:
         return 4.0 * self.inp.valid_pairs + 4.0 * self.inp.rows * self.inp.k
 
 
-def _time_steps(step, steps, warmup, record):
+def _time_steps(step, steps, warmup, record, cold=False):
     """Wall ms per step over `steps` timed steps; with record, per-launch and per-step HIP events
-    (on the launch stream) are kept on the step for the kernel times and the step distribution."""
+    (on the launch stream) are kept on the step for the kernel times and the step distribution.
+
+    cold: before every step a 512 MiB scratch buffer is rewritten (more than the 256 MB Infinity
+    Cache), so each step starts with cold caches; the flush lies outside the step events, and the
+    returned ms per step is then the mean of the step events instead of the wall time."""
     import torch
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if cold else None
     for _ in range(warmup):
         step.run()
     torch.cuda.synchronize()
     step.events = []
     step.step_events = []
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
+        if cold:
+            scratch.fill_(i & 0xff)
         if record:
             se = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             se[0].record()
@@ -229,6 +238,8 @@ def _time_steps(step, steps, warmup, record):
             se[1].record()
             step.step_events.append(se)
     torch.cuda.synchronize()
+    if cold and record:
+        return sum(e[0].elapsed_time(e[1]) for e in step.step_events) / steps
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
@@ -251,23 +262,29 @@ def _distribution(step):
 def measured_peaks():
     """On-box peaks next to the published ones.
 
-    mfma: the library's fp8 MFMA throughput probe (2 workgroups of 256 threads per CU, each wave
-    4 x 4096 back-to-back 16x16x128 fp8 MFMAs on four accumulators), HIP events around 5 launches.
+    mfma: the library's fp8 MFMA throughput probe (2 and 4 workgroups of 256 threads per CU, each wave
+    4 x 4096 back-to-back 16x16x128 fp8 MFMAs on four accumulators), HIP events around 5 launches;
+    the faster of the two.
     copy: a device-to-device copy of 1 GiB (torch copy_), read plus written bytes, 5 copies.
     """
     import torch
     import fp8_mqa_logits_amd as F
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    blocks, iters, reps = 2 * cus, 4096, 5
-    out, flops = F.fp8idx_probe_mfma_fp8(blocks, iters)
-    torch.cuda.synchronize()
+    iters, reps = 4096, 5
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        F.fp8idx_probe_mfma_fp8(blocks, iters, out=out)
-    e1.record()
-    torch.cuda.synchronize()
-    mfma_tflops = flops / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
+    mfma_tflops, best = 0.0, 0
+    for per_cu in (2, 4):
+        blocks = per_cu * cus
+        out, flops = F.fp8idx_probe_mfma_fp8(blocks, iters)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            F.fp8idx_probe_mfma_fp8(blocks, iters, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        t = flops / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
+        if t > mfma_tflops:
+            mfma_tflops, best = t, blocks
     nbytes = 1 << 30
     x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
     y = torch.empty_like(x)
@@ -282,7 +299,7 @@ def measured_peaks():
     del x, y, out
     torch.cuda.empty_cache()
     return {"mfma_fp8_tflops": round(mfma_tflops, 1), "copy_gbps": round(copy_gbps, 1),
-            "mfma_probe": f"{blocks} x 256 threads, 4 x {iters} fp8 16x16x128 MFMAs per wave, {reps} launches",
+            "mfma_probe": f"{best} x 256 threads, 4 x {iters} fp8 16x16x128 MFMAs per wave, {reps} launches",
             "copy_probe": f"1 GiB device copy, read + written bytes, {reps} copies"}
 
 
@@ -335,20 +352,30 @@ def _cpu_baseline(inp, budget_s):
         valid += int((inp.ke[rows].astype(np.int64) - inp.ks[rows]).clip(min=0).sum())
         done += rows.size
     tflops = 2.0 * H * D * valid / t_total / 1e12
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": f"{done} evenly spaced rows of {inp.m} ({valid} valid (row, key) pairs), "
                       f"float64 logits + top-k, {t_total:.1f} s; ms/layer-equivalent "
                       f"{t_total * 1e3 * inp.valid_pairs / max(valid, 1):.0f}"}
 
 
-def run_workload(name, steps, warmup, fused_check):
+def run_workload(name, steps, warmup, fused_check, cold=False):
     import torch
     from workloads.generate import config_inputs
     inp = config_inputs(name)
     paged = hasattr(inp, "kv_pool")
     step = PagedStep(inp) if paged else RaggedStep(inp)
     torch.cuda.synchronize()
-    ms = _time_steps(step, steps, warmup, record=True)
+    ms = _time_steps(step, steps, warmup, record=True, cold=cold)
     logit_ms, topk_ms, launches = step.kernel_times()
     per_step = launches // steps
     # per-launch averages times launches per step = kernel time per step (chunked workloads
@@ -618,7 +645,7 @@ def main():
             print(json.dumps(q), flush=True)
         return
 
-    r = run_workload(a.workload, a.steps, a.warmup, a.fused_check)
+    r = run_workload(a.workload, a.steps, a.warmup, a.fused_check, cold=a.cold)
     inp, step = r["inp"], r["step"]
     flops = r["flops"]
     logit_tflops = flops / (r["logits_ms"] * 1e-3) / 1e12
@@ -646,7 +673,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8",
         "data": "synthetic",
-        "config": {"workload": inp.name},
+        "config": {"workload": inp.name, "caches": "cold" if a.cold else "warm"},
         "roofline": roof,
         "logits_ms": round(r["logits_ms"], 4),
         "topk_ms": round(r["topk_ms"], 4),
