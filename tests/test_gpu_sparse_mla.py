@@ -1,6 +1,8 @@
 """Parity of the HIP sparse MLA attention (the consumer of the top-k slots) with the float64 oracle.
 
-Tolerance, from the arithmetic: the scores are exact bf16 x fp8 products summed in fp32; the
+Tolerance, from the arithmetic: the scores are exact bf16 x fp8 products summed in fp32 (the
+kernel's two-part e4m3 split of q is exact for every value above 2^-10 of its 32-value block
+maximum and off by at most 2^-17 of that maximum below it, far under this bound); the
 probabilities enter the value product rounded to bf16 (relative error <= 2^-9 each), so
 |o_gpu - o| <= 2^-9 * max |v| over the token's selected values; the test allows twice that.
 lse sees only fp32 accumulation and exp / log rounding: 1e-4 + 1e-5 |lse|.
@@ -107,3 +109,21 @@ def test_chained_after_the_oracle_top_k():
     mla.indices[:] = slots.astype(np.int32)
     o, lse = _run(mla)
     _check(mla, o, lse, list(range(slots.shape[0])), "chained")
+
+
+def test_q_blocks_of_very_different_magnitudes():
+    """q scaled by 2^-u per 16-value group (u in 0..16, exact in bf16): the per-block exponents of
+    the fp8 score path differ from block to block and between the two halves of a block, which
+    pins the block-to-scale-lane layout of the scaled MFMA."""
+    import dataclasses
+    inp = sparse_mla_inputs(3, 64, 700, 256, seed=11)
+    rng = np.random.default_rng(11)
+    qf = (inp.q_bits.astype(np.uint32) << 16).view(np.float32)
+    T, H, D = qf.shape
+    u = rng.integers(0, 17, size=(T, H, D // 16))
+    qf = qf * np.repeat(np.exp2(-u.astype(np.float64)), 16, axis=2).astype(np.float32)
+    q_bits = np.ascontiguousarray((qf.view(np.uint32) >> 16).astype(np.uint16))
+    assert np.array_equal((q_bits.astype(np.uint32) << 16).view(np.float32), qf)   # exact in bf16
+    inp = dataclasses.replace(inp, q_bits=q_bits)
+    o, lse = _run(inp)
+    _check(inp, o, lse, [0, 1, 2], "q block magnitudes")
