@@ -164,6 +164,10 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
       qr[j] = __builtin_bit_cast(v8bf, raw);
     }
   }
+  // The rotary q goes straight from its load into the step loop's MFMAs.  Without this wait the
+  // compiler's wait counter carries that load into the loop, merges it with the key gathers in
+  // flight at the loop's back edge, and waits for all of them (vmcnt(0)) in every step's scores.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), before any gather is issued
 
   // ---- staging: this thread's two latent chunks of a key quad, one rotary chunk, one scale
   const int sq = tid >> 4;            // keys 4 sq .. 4 sq + 3 of the step
