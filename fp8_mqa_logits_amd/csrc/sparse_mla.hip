@@ -168,6 +168,12 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
   // compiler's wait counter carries that load into the loop, merges it with the key gathers in
   // flight at the loop's back edge, and waits for all of them (vmcnt(0)) in every step's scores.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), before any gather is issued
+  // q's fp8 parts are only ever MFMA operands: placing them in accumulation registers frees 64
+  // VGPRs, which the score loop uses to load the next key fragment ahead of each MFMA pair.
+#pragma unroll
+  for (int c = 0; c < kLatChunks; ++c) {
+    asm volatile("; q parts to AGPRs" : "+a"(qh[c]), "+a"(ql[c]));
+  }
 
   // ---- staging: this thread's two latent chunks of a key quad, one rotary chunk, one scale
   const int sq = tid >> 4;            // keys 4 sq .. 4 sq + 3 of the step
@@ -236,16 +242,21 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
     v4f S[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) S[kt] = v4f{0.f, 0.f, 0.f, 0.f};
+    // the key fragment of the next MFMA pair is loaded before this pair is issued
+    auto kfrag = [&](int i) -> v8i {
+      const v4i* p = reinterpret_cast<const v4i*>(K + (16 * (i & 3) + l16) * kKRow + 128 * (i >> 2) + 32 * g);
+      const v4i w0 = p[0], w1 = p[1];
+      return v8i{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+    };
+    v8i kf = kfrag(0);
 #pragma unroll
-    for (int c = 0; c < kLatChunks; ++c) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const v4i* p = reinterpret_cast<const v4i*>(K + (16 * kt + l16) * kKRow + 128 * c + 32 * g);
-        const v4i w0 = p[0], w1 = p[1];
-        const v8i kf = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-        S[kt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qh[c], S[kt], 0, 0, 0, 127, 0, qsc[c]);
-        S[kt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, ql[c], S[kt], 0, 0, 0, 127, 0, qsc[c]);
-      }
+    for (int i = 0; i < 4 * kLatChunks; ++i) {
+      const int c = i >> 2, kt = i & 3;
+      v8i kn = kf;
+      if (i + 1 < 4 * kLatChunks) kn = kfrag(i + 1);
+      S[kt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, qh[c], S[kt], 0, 0, 0, 127, 0, qsc[c]);
+      S[kt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, ql[c], S[kt], 0, 0, 0, 127, 0, qsc[c]);
+      kf = kn;
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
