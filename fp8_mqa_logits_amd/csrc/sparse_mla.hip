@@ -318,15 +318,22 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
     // (2 t, 2 t + 1) of each 16 points at the t-th of those keys' row, columns 16 n and 16 n + 8.
     const int tkey = (l16 >> 1) < 4 ? 4 * g + (l16 >> 1) : 16 + 4 * g + (l16 >> 1) - 4;
     const uint8_t* vrow = K + tkey * kKRow + 8 * (l16 & 1);
+    // MFMA i: key step i / 32, value tile i % 32, so consecutive MFMAs update different tiles; the
+    // transpose reads run kVAhead MFMAs ahead.
+    typedef int v2i_t __attribute__((ext_vector_type(2)));
+    auto vfrag = [&](int i) -> v2i_t {
+      return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) v2i_t*)(vrow + 32 * (i / kVTiles) * kKRow + 16 * (i % kVTiles)));
+    };
+    constexpr int kVAhead = 4;
+    v2i_t vq[kVAhead];
 #pragma unroll
-    for (int n = 0; n < kVTiles; ++n) {
+    for (int j = 0; j < kVAhead; ++j) vq[j] = vfrag(j);
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        typedef int v2i_t __attribute__((ext_vector_type(2)));
-        const v2i_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i_t*)(vrow + 32 * ks2 * kKRow + 16 * n));
-        O[n] = mfma_bf16(P[ks2], fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]), O[n]);
-      }
+    for (int i = 0; i < 2 * kVTiles; ++i) {
+      const v2i_t w = vq[i % kVAhead];
+      if (i + kVAhead < 2 * kVTiles) vq[i % kVAhead] = vfrag(i + kVAhead);
+      O[i % kVTiles] = mfma_bf16(P[i / kVTiles], fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]), O[i % kVTiles]);
     }
 
   };
