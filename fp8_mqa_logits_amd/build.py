@@ -38,6 +38,15 @@ HIP_FLAGS = [
 ]
 
 
+# Per-source extra flags.  sparse_mla.hip: MFMA accumulators in VGPRs.  Its 16 x 512 output per
+# wave is carried from step to step; in the default AGPR form the compiler gave each value MFMA a
+# destination other than its accumulator input and copied all 128 output registers through VGPRs
+# in every step, which the VGPR form avoids (the kernel runs one wave per SIMD and has the room).
+FILE_FLAGS = {
+    "sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -51,7 +60,7 @@ def sources():
 
 def _compile(hipcc: str, src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc, *HIP_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc, *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
