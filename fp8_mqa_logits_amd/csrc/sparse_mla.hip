@@ -329,11 +329,19 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
     v2i_t vq[kVAhead];
 #pragma unroll
     for (int j = 0; j < kVAhead; ++j) vq[j] = vfrag(j);
+    // the widened operand of MFMA i + 1 is formed before MFMA i is issued
+    v8bf vb = fp8x8_to_bf16((uint32_t)vq[0][0], (uint32_t)vq[0][1]);
+    vq[0] = vfrag(kVAhead);
 #pragma unroll
     for (int i = 0; i < 2 * kVTiles; ++i) {
-      const v2i_t w = vq[i % kVAhead];
-      if (i + kVAhead < 2 * kVTiles) vq[i % kVAhead] = vfrag(i + kVAhead);
-      O[i % kVTiles] = mfma_bf16(P[i / kVTiles], fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]), O[i % kVTiles]);
+      v8bf vn = vb;
+      if (i + 1 < 2 * kVTiles) {
+        const v2i_t w = vq[(i + 1) % kVAhead];
+        if (i + 1 + kVAhead < 2 * kVTiles) vq[(i + 1) % kVAhead] = vfrag(i + 1 + kVAhead);
+        vn = fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
+      }
+      O[i % kVTiles] = mfma_bf16(P[i / kVTiles], vb, O[i % kVTiles]);
+      vb = vn;
     }
 
   };
