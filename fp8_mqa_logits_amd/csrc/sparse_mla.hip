@@ -258,14 +258,18 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
       S[kt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf, ql[c], S[kt], 0, 0, 0, 127, 0, qsc[c]);
       kf = kn;
     }
+    // rotary: the eight 8-byte key slices load together; each is widened one MFMA ahead
+    uint2 rw[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int i = 0; i < 8; ++i)
+      rw[i] = *reinterpret_cast<const uint2*>(K + (16 * (i & 3) + l16) * kKRow + kMlaDv + 32 * (i >> 2) + 8 * g);
+    v8bf rb = fp8x8_to_bf16(rw[0].x, rw[0].y);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const uint8_t* p = K + (16 * kt + l16) * kKRow + kMlaDv + 32 * j + 8 * g;
-        const uint2 w = *reinterpret_cast<const uint2*>(p);
-        S[kt] = mfma_bf16(fp8x8_to_bf16(w.x, w.y), qr[j], S[kt]);
-      }
+    for (int i = 0; i < 8; ++i) {
+      v8bf rn = rb;
+      if (i + 1 < 8) rn = fp8x8_to_bf16(rw[i + 1].x, rw[i + 1].y);
+      S[i & 3] = mfma_bf16(rb, qr[i >> 2], S[i & 3]);
+      rb = rn;
     }
 
     // to log2 units, masked keys to -inf; the step's maximum per head
