@@ -392,27 +392,52 @@ __global__ __launch_bounds__(kMlaThreads, 1) void sparse_mla_kernel(SparseMlaArg
 }
 
 // Merges the splits of each (token, head): weights exp(lse_s - lse), lse = log sum exp(lse_s).
-__global__ __launch_bounds__(128) void sparse_mla_combine_kernel(SparseMlaArgs a, int nsplit, const float* part_o,
-                                                                 const float* part_lse) {
+constexpr int kCombineThreads = kMlaDv / 4;   // 128: one float4 of the 512 outputs each
+constexpr int kCombineChunk = 256;            // split weights held in LDS at a time
+
+// One workgroup per (token, head): the splits' lse values are read together, their weights
+// exp(lse_s - max) kept in LDS (kCombineChunk splits at a time), and the outputs summed over the
+// splits in split order with several partial rows in flight.
+__global__ __launch_bounds__(kCombineThreads) void sparse_mla_combine_kernel(SparseMlaArgs a, int nsplit,
+                                                                           const float* part_o,
+                                                                           const float* part_lse) {
+  __shared__ float s_w[kCombineChunk];
+  __shared__ float s_red[kCombineThreads / 64];
   const int t = blockIdx.x;
   const int head = blockIdx.y;
+  const int tid = threadIdx.x;
+  const float* lse_th = part_lse + (int64_t)t * nsplit * a.H + head;   // split s at lse_th[s * H]
   float m = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_lse[((int64_t)t * nsplit + s) * a.H + head]);
+  for (int s = tid; s < nsplit; s += kCombineThreads) m = fmaxf(m, lse_th[(int64_t)s * a.H]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((tid & 63) == 0) s_red[tid >> 6] = m;
+  __syncthreads();
+  m = fmaxf(s_red[0], s_red[1]);
   float z = 0.f;
   v4f acc = {0.f, 0.f, 0.f, 0.f};
-  if (m != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float ls = part_lse[((int64_t)t * nsplit + s) * a.H + head];
-      const float w = ls == -INFINITY ? 0.f : __expf(ls - m);
-      z += w;
-      const v4f v = *reinterpret_cast<const v4f*>(part_o + (((int64_t)t * nsplit + s) * a.H + head) * kMlaDv +
-                                                  4 * threadIdx.x);
-      acc += v * w;
+  const float* po = part_o + ((int64_t)t * nsplit * a.H + head) * kMlaDv + 4 * tid;
+  const int64_t stride = (int64_t)a.H * kMlaDv;
+  for (int b = 0; b < nsplit; b += kCombineChunk) {
+    const int nb = min(kCombineChunk, nsplit - b);
+    for (int s = tid; s < nb; s += kCombineThreads) {
+      const float ls = lse_th[(int64_t)(b + s) * a.H];
+      s_w[s] = (m == -INFINITY || ls == -INFINITY) ? 0.f : __expf(ls - m);
     }
+    __syncthreads();
+    if (m != -INFINITY) {
+#pragma unroll 8
+      for (int s = 0; s < nb; ++s) {
+        const float w = s_w[s];
+        z += w;
+        acc += *reinterpret_cast<const v4f*>(po + (int64_t)(b + s) * stride) * w;
+      }
+    }
+    __syncthreads();   // the next chunk rewrites s_w
   }
   const float inv = z > 0.f ? 1.f / z : 0.f;
-  *reinterpret_cast<v4f*>(a.out + ((int64_t)t * a.H + head) * kMlaDv + 4 * threadIdx.x) = acc * inv;
-  if (threadIdx.x == 0 && a.lse) a.lse[(int64_t)t * a.H + head] = z > 0.f ? m + __logf(z) : -INFINITY;
+  *reinterpret_cast<v4f*>(a.out + ((int64_t)t * a.H + head) * kMlaDv + 4 * tid) = acc * inv;
+  if (tid == 0 && a.lse) a.lse[(int64_t)t * a.H + head] = z > 0.f ? m + __logf(z) : -INFINITY;
 }
 
 // Splits each top-k list so that about kMlaTargetWgs workgroups run (one per
@@ -450,7 +475,7 @@ hipError_t launch_sparse_mla(const SparseMlaArgs& a, const SparseMlaPlan& plan, 
                      plan.keys_per_split, part_o, part_lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.nsplit == 1) return e;
-  hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3((unsigned)a.T, (unsigned)a.H), dim3(kMlaDv / 4), 0, s, a,
+  hipLaunchKernelGGL(sparse_mla_combine_kernel, dim3((unsigned)a.T, (unsigned)a.H), dim3(kCombineThreads), 0, s, a,
                      plan.nsplit, part_o, part_lse);
   return hipGetLastError();
 }

@@ -127,3 +127,12 @@ def test_q_blocks_of_very_different_magnitudes():
     inp = dataclasses.replace(inp, q_bits=q_bits)
     o, lse = _run(inp)
     _check(inp, o, lse, [0, 1, 2], "q block magnitudes")
+
+
+def test_more_splits_than_one_combine_chunk():
+    """540000 slots for one token: 2048-slot splits give 264 of them, more than the 256 split
+    weights the combine holds in LDS at once, so the combine runs in two chunks."""
+    inp = sparse_mla_inputs(1, 16, 500, 540000, seed=21)
+    assert F.fp8idx_sparse_mla_workspace_bytes(1, 16, 540000) == 264 * 16 * 513 * 4 + 256
+    o, lse = _run(inp)
+    _check(inp, o, lse, [0], "264 splits")
