@@ -25,7 +25,10 @@ Readings where the pages are silent (each is also listed in the design notes):
 * ragged token-table position of key j for row i is ``j - ks[i]`` in the
   row's request (request found from ``cu_rows``);
 * paged decode: key j of request b lives in physical slot
-  ``block_table[b, j // page] * page + j % page``.
+  ``block_table[b, j // page] * page + j % page``; a key whose page id lies
+  outside the pool [0, pages) holds no kv (block tables carry -1 past a
+  request's pages), so its logit is -inf and, when the top-k takes it (a row
+  with fewer than k real keys), it maps to -1 like the padding.
 
 Exactness: every e4m3fn code is an integer multiple of 2**-9 with magnitude
 at most 448, so every product q*kv is a multiple of 2**-18 and a sum of 128
@@ -225,12 +228,19 @@ def mqa_logits(q: np.ndarray, kv: np.ndarray, kv_scale: np.ndarray, weights: np.
 
 def gather_paged_kv(kv_pool: np.ndarray, scale_pool: np.ndarray, block_table_row: np.ndarray,
                     length: int, page_size: int):
-    """Contiguous (kv codes [length, D], scales [length]) of one request's keys."""
+    """Contiguous (kv codes [length, D], scales [length], real [length]) of one request's keys.
+
+    real[j] is False for keys on a page id outside [0, pages); their kv and
+    scale are placeholders (page 0) that the caller must not score.
+    """
     pages = (int(length) + page_size - 1) // page_size
     phys = np.asarray(block_table_row[:pages], dtype=np.int64)
+    ok = (phys >= 0) & (phys < kv_pool.shape[0])
+    phys = np.where(ok, phys, 0)
     kv = kv_pool[phys].reshape(pages * page_size, kv_pool.shape[-1])[:length]
     sc = scale_pool[phys].reshape(pages * page_size)[:length]
-    return kv, sc
+    real = np.repeat(ok, page_size)[:length]
+    return kv, sc, real
 
 
 def paged_mqa_logits(q: np.ndarray, kv_pool: np.ndarray, scale_pool: np.ndarray,
@@ -240,9 +250,9 @@ def paged_mqa_logits(q: np.ndarray, kv_pool: np.ndarray, scale_pool: np.ndarray,
     """Paged-decode logits, float64 [len(rows), width].
 
     q uint8 [B, next_n, H, D]; row r = b * next_n + t sees keys [0, row_len[r])
-    of request b, whose key j is kv_pool[block_table[b, j // page], j % page].
-    ``rows`` selects a subset of rows (default: all); ``width`` defaults to
-    max(row_len).
+    of request b, whose key j is kv_pool[block_table[b, j // page], j % page]
+    (-inf for a key whose page id lies outside the pool).  ``rows`` selects a
+    subset of rows (default: all); ``width`` defaults to max(row_len).
     """
     B, nn, Hh, Dd = q.shape
     row_len = np.asarray(row_len, dtype=np.int64)
@@ -255,9 +265,10 @@ def paged_mqa_logits(q: np.ndarray, kv_pool: np.ndarray, scale_pool: np.ndarray,
         L = int(row_len[r])
         if L <= 0:
             continue
-        kv_b, sc_b = gather_paged_kv(kv_pool, scale_pool, block_table[b], L, page_size)
+        kv_b, sc_b, real = gather_paged_kv(kv_pool, scale_pool, block_table[b], L, page_size)
         out[o] = mqa_logits(qf[r:r + 1], kv_b, sc_b, weights[r:r + 1],
                             np.zeros(1, np.int64), np.array([L]), width=width)[0]
+        out[o, :L][~real[:width]] = -np.inf
     return out
 
 
@@ -308,15 +319,21 @@ def map_token_table(raw: np.ndarray, rows: Sequence[int], ks: np.ndarray,
 
 
 def map_block_table(raw: np.ndarray, rows: Sequence[int], next_n: int,
-                    block_table: np.ndarray, page_size: int) -> np.ndarray:
-    """Paged map: raw key j of row r -> block_table[r // next_n, j // page] * page + j % page."""
+                    block_table: np.ndarray, page_size: int, num_pages: Optional[int] = None) -> np.ndarray:
+    """Paged map: raw key j of row r -> block_table[r // next_n, j // page] * page + j % page.
+
+    A page id outside [0, num_pages) (any negative id when num_pages is None)
+    maps to -1, as does -1 padding.
+    """
     raw = np.asarray(raw, dtype=np.int64)
     out = np.full(raw.shape, -1, dtype=np.int64)
     for o, r in enumerate(rows):
         b = int(r) // int(next_n)
         sel = raw[o] >= 0
         j = raw[o, sel]
-        out[o, sel] = block_table[b, j // page_size].astype(np.int64) * page_size + j % page_size
+        page = block_table[b, j // page_size].astype(np.int64)
+        real = (page >= 0) & (page < (num_pages if num_pages is not None else np.iinfo(np.int64).max))
+        out[o, sel] = np.where(real, page * page_size + j % page_size, -1)
     return out
 
 
@@ -338,7 +355,7 @@ def paged_topk_mapped(inp, rows: Optional[Sequence[int]] = None, width: Optional
                          inp.block_table, inp.page_size, width=width, rows=rows)
     ridx = np.asarray(rows, dtype=np.int64)
     raw = topk_indices(L, np.zeros(len(rows), np.int64), inp.row_len[ridx], inp.k)
-    mapped = map_block_table(raw, rows, inp.next_n, inp.block_table, inp.page_size)
+    mapped = map_block_table(raw, rows, inp.next_n, inp.block_table, inp.page_size, inp.kv_pool.shape[0])
     return L, raw, mapped
 
 

@@ -58,8 +58,41 @@ def test_paged_equals_ragged_on_hand_gathered_kv():
 
 def test_gather_paged_kv_contiguity():
     inp = paged_inputs(2, 1, 100, 200, 8, seed=23, page_size=64)
-    kv, sc = gather_paged_kv(inp.kv_pool, inp.scale_pool, inp.block_table[1], int(inp.ctx[1]), 64)
+    kv, sc, real = gather_paged_kv(inp.kv_pool, inp.scale_pool, inp.block_table[1], int(inp.ctx[1]), 64)
     assert kv.shape == (int(inp.ctx[1]), D)
+    assert real.all()
     j = int(inp.ctx[1]) - 1
     assert np.array_equal(kv[j], inp.kv_pool[inp.block_table[1, j // 64], j % 64])
     assert sc[j] == inp.scale_pool[inp.block_table[1, j // 64], j % 64]
+
+
+def test_paged_invalid_pages_bruteforce():
+    """A key on a page id outside the pool (-1 past a request's pages, or an id past the last page)
+    has no kv: its logit is -inf; every other key is the formula, evaluated here one key at a time
+    from torch's fp8 decode with a scalar epilogue."""
+    from tests.oracle_pins import torch_decode
+    inp = paged_inputs(2, 2, 150, 260, 8, seed=24, page_size=64)
+    P = inp.kv_pool.shape[0]
+    bt = inp.block_table.copy()
+    bt[0, 1] = -1          # a hole inside request 0's window
+    bt[1, 0] = P           # one past the last page
+    bt[1, 2] = P + 7
+    L = paged_mqa_logits(inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len, bt, 64)
+    Q = torch_decode(inp.q).reshape(inp.rows, H, D)
+    K = torch_decode(inp.kv_pool)
+    for r in range(inp.rows):
+        b = r // inp.next_n
+        n_r = int(inp.row_len[r])
+        for j in range(n_r):
+            page = int(bt[b, j // 64])
+            if page < 0 or page >= P:
+                assert L[r, j] == -np.inf, (r, j)
+                continue
+            k = K[page, j % 64]
+            sc = float(inp.scale_pool[page, j % 64])
+            want = 0.0
+            for h in range(H):
+                x = float(np.dot(Q[r, h], k)) * sc
+                want += float(inp.weights[r, h]) * max(x, 0.0)
+            assert abs(L[r, j] - want) <= 1e-12 * max(1.0, abs(want)), (r, j)
+        assert np.all(L[r, n_r:] == -np.inf)

@@ -122,6 +122,21 @@ def test_paged_mapped_pipeline_small():
         assert np.array_equal(mapped[r], inp.block_table[b, j // 64].astype(np.int64) * 64 + j % 64)
 
 
+def test_block_table_invalid_pages_map_to_minus_one():
+    """Page ids outside [0, num_pages) map to -1; a row whose keys are all on such pages is all -inf,
+    its top-k takes the lowest positions (ties by index) and every one maps to -1."""
+    bt = np.array([[5, -1, 9, 12]], dtype=np.int32)
+    raw = np.array([[0, 63, 64, 127, 128, 191, 192, -1]])
+    got = map_block_table(raw, [0], 1, bt, 64, num_pages=10)
+    assert got.tolist() == [[5 * 64, 5 * 64 + 63, -1, -1, 9 * 64, 9 * 64 + 63, -1, -1]]
+    # without a page count only negative ids are invalid
+    assert map_block_table(raw, [0], 1, bt, 64)[0, 6] == 12 * 64
+    L = np.full((1, 100), -np.inf)
+    sel = topk_indices(L, np.zeros(1, np.int64), np.array([100]), 8)
+    assert sel.tolist() == [list(range(8))]
+    assert np.all(map_block_table(sel, [0], 1, np.full((1, 2), -1, np.int32), 64, num_pages=10) == -1)
+
+
 def test_rows_per_chunk_chunking_page_formula():
     # max(1, int(gb * 1e9) // (n * 4)) rows per chunk, decimal gigabytes
     assert rows_per_chunk(2_000_000_000, 210000, 7500) == 2380
