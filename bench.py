@@ -95,6 +95,7 @@ class RaggedStep:
         self.logits = torch.empty((self.rpc, self.ld), dtype=torch.float32, device="cuda")
         tk = F.fp8idx_workspace_bytes(F.OP_TOPK, self.rpc, n, k, 0)
         self.ws_topk = torch.empty(max(tk, 1) + 256, dtype=torch.uint8, device="cuda")
+        self.ws_logits = torch.empty(512, dtype=torch.uint8, device="cuda")
         self.out = torch.empty((m, k), dtype=torch.int32, device="cuda")
         fws = F.fp8idx_workspace_bytes(F.OP_LOGITS_TOPK_RAGGED, m, n, k, self.cap)
         self.fused_ws = None
@@ -112,7 +113,7 @@ class RaggedStep:
                 ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
                 ev[0].record()
             F.indexer_logits_ragged(self.q[s:e], self.kv, self.sc, self.w[s:e], self.ks[s:e], self.ke[s:e],
-                                    clean=False, logits=self.logits[: e - s])
+                                    clean=False, logits=self.logits[: e - s], workspace=self.ws_logits)
             if record:
                 ev[1].record()
             F.indexer_topk(self.logits[: e - s], self.ke[s:e], inp.k, ks=self.ks[s:e], width=inp.n, row0=s,
@@ -168,7 +169,8 @@ class PagedStep:
         tk = F.fp8idx_workspace_bytes(F.OP_TOPK, inp.rows, self.width, inp.k, 0)
         self.ws_topk = torch.empty(max(tk, 1) + 256, dtype=torch.uint8, device="cuda")
         self.out = torch.empty((inp.rows, inp.k), dtype=torch.int32, device="cuda")
-        m = F.TopkMap(kind=F.MAP_BLOCK_TABLE, table=self.args[5], rows_per_req=inp.next_n, page_size=64)
+        m = F.TopkMap(kind=F.MAP_BLOCK_TABLE, table=self.args[5], rows_per_req=inp.next_n, page_size=64,
+                      num_pages=inp.kv_pool.shape[0])
         self.map = m
         self.fused_ws_bytes = F.fp8idx_workspace_bytes_paged(inp.B, inp.next_n, self.width, inp.k, 0)
         self.fused_ws = None

@@ -14,6 +14,15 @@ from .binding import (  # noqa: F401
     OP_TOPK,
     OP_LOGITS_TOPK_RAGGED,
     OP_LOGITS_TOPK_RAGGED_OVERLAP,
+    OP_LOGITS_RAGGED,
+    ENTRY_LOGITS_RAGGED,
+    ENTRY_LOGITS_PAGED,
+    ENTRY_TOPK,
+    ENTRY_LOGITS_TOPK_RAGGED,
+    ENTRY_LOGITS_TOPK_RAGGED_OVERLAP,
+    ENTRY_LOGITS_TOPK_PAGED,
+    CallArgs,
+    fp8idx_validate_only,
     LIB_PATH,
     load_library,
     indexer_logits_ragged,

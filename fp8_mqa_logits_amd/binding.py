@@ -1,9 +1,11 @@
 """ctypes binding of libfp8idx.so, the C ABI declared in include/fp8idx.h.
 
-Argument marshalling only: each function checks dtypes, devices and
-contiguity of torch tensors, takes their device pointers and the current
-HIP stream, calls the C entry point of the same name and raises
-``Fp8idxError`` on a non-OK status.  Output and workspace tensors the caller
+Argument marshalling only: each function checks the dtype, shape (or
+element count), contiguity and device of every torch tensor against the
+sizes the call implies (the C ABI takes bare pointers and cannot see how
+large a buffer is), raising ``ValueError`` before anything is launched; it
+then takes their device pointers and the current HIP stream, calls the C
+entry point of the same name and raises ``Fp8idxError`` on a non-OK status.  Output and workspace tensors the caller
 does not pass are allocated here with torch (device memory is the only thing
 torch provides); every step of the computation runs in the library's HIP
 kernels.  There is no fallback: if the library is not built, or the device
@@ -26,7 +28,9 @@ D = 128
 
 STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "EDEVICE", 5: "EHIP"}
 MAP_NONE, MAP_TOKEN_TABLE, MAP_BLOCK_TABLE = 0, 1, 2
-OP_TOPK, OP_LOGITS_TOPK_RAGGED, OP_LOGITS_TOPK_RAGGED_OVERLAP = 0, 1, 2
+OP_TOPK, OP_LOGITS_TOPK_RAGGED, OP_LOGITS_TOPK_RAGGED_OVERLAP, OP_LOGITS_RAGGED = 0, 1, 2, 3
+(ENTRY_LOGITS_RAGGED, ENTRY_LOGITS_PAGED, ENTRY_TOPK, ENTRY_LOGITS_TOPK_RAGGED,
+ ENTRY_LOGITS_TOPK_RAGGED_OVERLAP, ENTRY_LOGITS_TOPK_PAGED) = range(6)
 
 EXPORTED = (
     "indexer_logits_ragged", "indexer_logits_paged", "indexer_topk",
@@ -36,6 +40,7 @@ EXPORTED = (
     "indexer_quant_fp8", "indexer_logits_topk_ragged_overlap",
     "indexer_prepare_ragged", "indexer_prepare_decode",
     "indexer_sparse_mla", "fp8idx_sparse_mla_workspace_bytes", "fp8idx_probe_mfma_fp8",
+    "fp8idx_validate_only",
 )
 
 MLA_DQK = 576   # sparse MLA KV row: 512 latent + 64 rotary values
@@ -57,6 +62,25 @@ class _CMap(ctypes.Structure):
         ("cu_rows", ctypes.c_void_p),
         ("rows_per_req", ctypes.c_int32),
         ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+    ]
+
+
+class CallArgs(ctypes.Structure):
+    """fp8idx_call_args: the arguments of one indexer call, for fp8idx_validate_only()."""
+
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("kv", ctypes.c_void_p), ("kv_scale", ctypes.c_void_p),
+        ("weights", ctypes.c_void_p), ("ks", ctypes.c_void_p), ("ke", ctypes.c_void_p),
+        ("row_len", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+        ("m", ctypes.c_int32), ("n", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("next_n", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32), ("num_pages", ctypes.c_int64), ("width", ctypes.c_int32),
+        ("logits", ctypes.c_void_p), ("scores", ctypes.c_void_p), ("ld_logits", ctypes.c_int64),
+        ("clean", ctypes.c_int32), ("rows", ctypes.c_int32), ("k", ctypes.c_int32), ("row0", ctypes.c_int32),
+        ("map_to_slots", ctypes.c_int32), ("map", ctypes.c_void_p), ("out", ctypes.c_void_p),
+        ("ld_out", ctypes.c_int64), ("logits_cap_bytes", ctypes.c_size_t), ("ws", ctypes.c_void_p),
+        ("ws_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p), ("side_stream", ctypes.c_void_p),
     ]
 
 
@@ -79,7 +103,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "(or __graft_entry__.build()) first")
     L = ctypes.CDLL(path)
     sig = {
-        "indexer_logits_ragged": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _I64, _I32, _P]),
+        "indexer_logits_ragged": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _I64, _I32,
+                                         _P, _SZ, _P]),
         "indexer_logits_paged": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I64,
                                         _P, _I64, _I32, _I32, _P]),
         "indexer_topk": (_I32, [_P, _I64, _I32, _I32, _P, _P, _I32, _I32, ctypes.POINTER(_CMap), _P, _I64,
@@ -103,6 +128,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       _P, _P, _P, _SZ, _P]),
         "fp8idx_sparse_mla_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
         "fp8idx_probe_mfma_fp8": (_I32, [_I32, _I32, _P, ctypes.POINTER(ctypes.c_double), _P]),
+        "fp8idx_validate_only": (_I32, [_I32, ctypes.POINTER(CallArgs)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -139,19 +165,38 @@ def _dev(t: torch.Tensor, name: str) -> torch.device:
     return t.device
 
 
-def _need(t: torch.Tensor, name: str, dtypes, dev: torch.device) -> torch.Tensor:
+def _same_device(dev: torch.device, **tensors) -> None:
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _need(t: torch.Tensor, name: str, dtypes, dev: Optional[torch.device] = None) -> torch.Tensor:
+    """dtype and contiguity (and, with dev, the device) of one tensor."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
     if t.dtype not in dtypes:
         raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
-    if t.device != dev:
+    if dev is not None and t.device != dev:
         raise ValueError(f"{name} is on {t.device}, expected {dev}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
 
 
-def _fp8(t: torch.Tensor, name: str, dev: torch.device) -> torch.Tensor:
+def _fp8(t: torch.Tensor, name: str, dev: Optional[torch.device] = None) -> torch.Tensor:
     _need(t, name, (torch.uint8, torch.float8_e4m3fn), dev)
     return t.view(torch.uint8) if t.dtype != torch.uint8 else t
+
+
+def _shape(t: torch.Tensor, name: str, shape) -> None:
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _numel(t: torch.Tensor, name: str, n: int) -> None:
+    if t.dim() != 1 or t.numel() != n:
+        raise ValueError(f"{name} must be 1-D with {n} elements, got shape {tuple(t.shape)}")
 
 
 _F32 = (torch.float32,)
@@ -160,29 +205,51 @@ _I32T = (torch.int32,)
 
 @dataclasses.dataclass
 class TopkMap:
-    """Index map of the top-k stage (fp8idx_map): kind, table [num_req, ld] int32 and extras."""
+    """Index map of the top-k stage (fp8idx_map): kind, table [num_req, ld] int32 and extras.
+
+    Block table: ``num_pages`` is the pool's page count (page ids outside [0, num_pages) map to -1).
+    """
 
     kind: int = MAP_NONE
     table: Optional[torch.Tensor] = None
     cu_rows: Optional[torch.Tensor] = None
     rows_per_req: int = 1
     page_size: int = 1
+    num_pages: int = 0
+
+    def check(self) -> None:
+        """Shapes and dtypes of the map's tensors (raises ValueError)."""
+        if self.kind not in (MAP_NONE, MAP_TOKEN_TABLE, MAP_BLOCK_TABLE):
+            raise ValueError(f"unknown map kind {self.kind}")
+        if self.kind == MAP_NONE:
+            return
+        if self.table is None:
+            raise ValueError("a token or block table map needs a table")
+        if self.table.dtype != torch.int32 or not self.table.is_contiguous() or self.table.dim() != 2:
+            raise ValueError("map table must be a contiguous 2-D int32 tensor")
+        if self.cu_rows is not None:
+            if self.cu_rows.dtype != torch.int32 or not self.cu_rows.is_contiguous():
+                raise ValueError("cu_rows must be a contiguous int32 tensor")
+            _numel(self.cu_rows, "cu_rows", self.table.shape[0] + 1)
+        if self.kind == MAP_BLOCK_TABLE:
+            if self.rows_per_req < 1 or self.page_size < 1:
+                raise ValueError("block table map needs rows_per_req >= 1 and page_size >= 1")
+            if self.num_pages < 1:
+                raise ValueError("block table map needs num_pages (pages in the pool) >= 1")
 
     def to_c(self) -> _CMap:
+        self.check()
         m = _CMap()
         m.kind = self.kind
         if self.table is not None:
-            if self.table.dtype != torch.int32 or not self.table.is_contiguous() or self.table.dim() != 2:
-                raise ValueError("map table must be a contiguous 2-D int32 tensor")
             m.table = self.table.data_ptr()
             m.ld = self.table.shape[1]
             m.num_req = self.table.shape[0]
         if self.cu_rows is not None:
-            if self.cu_rows.dtype != torch.int32 or not self.cu_rows.is_contiguous():
-                raise ValueError("cu_rows must be a contiguous int32 tensor")
             m.cu_rows = self.cu_rows.data_ptr()
         m.rows_per_req = self.rows_per_req
         m.page_size = self.page_size
+        m.num_pages = self.num_pages
         return m
 
 
@@ -190,6 +257,11 @@ def _cmap(map_: Optional[TopkMap]):
     if map_ is None:
         return None
     return ctypes.byref(map_.to_c())
+
+
+def _map_devices(map_: Optional[TopkMap], dev: torch.device) -> None:
+    if map_ is not None:
+        _same_device(dev, table=map_.table, cu_rows=map_.cu_rows)
 
 
 # ---------------------------------------------------------------------------
@@ -212,6 +284,11 @@ def fp8idx_version() -> str:
     return load_library().fp8idx_version().decode()
 
 
+def fp8idx_validate_only(entry: int, args: CallArgs) -> int:
+    """Status the entry would return for these arguments before looking for a device (host only)."""
+    return int(load_library().fp8idx_validate_only(int(entry), ctypes.byref(args)))
+
+
 def _workspace(nbytes: int, dev: torch.device, ws: Optional[torch.Tensor]):
     if nbytes == 0:
         return None, 0
@@ -221,7 +298,65 @@ def _workspace(nbytes: int, dev: torch.device, ws: Optional[torch.Tensor]):
         raise ValueError("workspace must be a contiguous uint8 device tensor")
     off = (-ws.data_ptr()) % 256
     avail = ws.numel() - off
-    return ws.data_ptr() + off, max(0, avail)
+    if avail < nbytes:
+        raise ValueError(f"workspace too small: {max(0, avail)} usable bytes after 256-byte alignment, "
+                         f"{nbytes} needed")
+    return ws.data_ptr() + off, avail
+
+
+def _ragged_inputs(q, kv, kv_scale, weights, ks, ke):
+    """Checks of the ragged logits inputs; returns (q8, kv8, m, n)."""
+    q8 = _fp8(q, "q")
+    kv8 = _fp8(kv, "kv")
+    if q8.dim() != 3 or q8.shape[1:] != (H, D):
+        raise ValueError(f"q must be [m, {H}, {D}], got {tuple(q8.shape)}")
+    if kv8.dim() != 2 or kv8.shape[1] != D:
+        raise ValueError(f"kv must be [n, {D}], got {tuple(kv8.shape)}")
+    m, n = q8.shape[0], kv8.shape[0]
+    _need(kv_scale, "kv_scale", _F32)
+    _numel(kv_scale, "kv_scale", n)
+    _need(weights, "weights", _F32)
+    _shape(weights, "weights", (m, H))
+    _need(ks, "ks", _I32T)
+    _numel(ks, "ks", m)
+    _need(ke, "ke", _I32T)
+    _numel(ke, "ke", m)
+    return q8, kv8, m, n
+
+
+def _paged_inputs(q, kv_pool, scale_pool, weights, row_len, block_table, width: int):
+    """Checks of the paged logits inputs; returns (q8, pool8, B, next_n)."""
+    q8 = _fp8(q, "q")
+    pool8 = _fp8(kv_pool, "kv_pool")
+    if q8.dim() != 4 or q8.shape[2:] != (H, D):
+        raise ValueError(f"q must be [B, next_n, {H}, {D}], got {tuple(q8.shape)}")
+    if pool8.dim() != 3 or pool8.shape[2] != D:
+        raise ValueError(f"kv_pool must be [pages, page_size, {D}], got {tuple(pool8.shape)}")
+    B, nn = q8.shape[0], q8.shape[1]
+    pages, page = pool8.shape[0], pool8.shape[1]
+    _need(scale_pool, "scale_pool", _F32)
+    if scale_pool.numel() != pages * page:
+        raise ValueError(f"scale_pool must hold pages * page_size = {pages * page} floats, "
+                         f"got {scale_pool.numel()}")
+    _need(weights, "weights", _F32)
+    _shape(weights, "weights", (B * nn, H))
+    _need(row_len, "row_len", _I32T)
+    _numel(row_len, "row_len", B * nn)
+    _need(block_table, "block_table", _I32T)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B = {B}, max_pages], got {tuple(block_table.shape)}")
+    if int(width) < 0 or int(width) > block_table.shape[1] * page:
+        raise ValueError(f"width must lie in [0, max_pages * page_size = {block_table.shape[1] * page}]")
+    return q8, pool8, B, nn
+
+
+def _out_rows(out: Optional[torch.Tensor], rows: int, k: int, dev) -> torch.Tensor:
+    if out is None:
+        return torch.empty((rows, k), dtype=torch.int32, device=dev)
+    _need(out, "out", _I32T)
+    if out.dim() != 2 or out.shape[0] != rows or out.shape[1] < k:
+        raise ValueError(f"out must be [{rows}, >= {k}] int32, got {tuple(out.shape)}")
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -229,26 +364,31 @@ def _workspace(nbytes: int, dev: torch.device, ws: Optional[torch.Tensor]):
 # ---------------------------------------------------------------------------
 
 def indexer_logits_ragged(q, kv, kv_scale, weights, ks, ke, *, clean: bool = True,
-                          logits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Ragged-prefill logits [m, n] float32 (or into ``logits`` [m, ld >= n])."""
-    dev = _dev(q, "q")
-    q8 = _fp8(q, "q", dev)
-    kv8 = _fp8(kv, "kv", dev)
-    m, n = q8.shape[0], kv8.shape[0]
-    if q8.shape[1:] != (H, D) or kv8.shape[1:] != (D,):
-        raise ValueError("q must be [m, 32, 128] and kv [n, 128]")
-    _need(kv_scale, "kv_scale", _F32, dev)
-    _need(weights, "weights", _F32, dev)
-    _need(ks, "ks", _I32T, dev)
-    _need(ke, "ke", _I32T, dev)
+                          logits: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
+    """Ragged-prefill logits [m, n] float32 (or into ``logits`` [m, ld >= n]).
+
+    ``workspace`` (uint8) holds the launch's work-queue counters: fp8idx_workspace_bytes(OP_LOGITS_RAGGED,
+    ...) = 256 bytes from its first 256-byte aligned address on.  One is allocated when it is not
+    given.  Calls that may run at the same time need distinct workspaces.
+    """
+    q8, kv8, m, n = _ragged_inputs(q, kv, kv_scale, weights, ks, ke)
+    if logits is not None:
+        _need(logits, "logits", _F32)
+        if logits.dim() != 2 or logits.shape[0] != m or logits.shape[1] < n:
+            raise ValueError(f"logits must be [{m}, >= {n}] float32, got {tuple(logits.shape)}")
+    dev = _dev(q8, "q")
+    _same_device(dev, kv=kv8, kv_scale=kv_scale, weights=weights, ks=ks, ke=ke, logits=logits,
+                 workspace=workspace)
     if logits is None:
         logits = torch.empty((m, n), dtype=torch.float32, device=dev)
-    else:
-        _need(logits, "logits", _F32, dev)
+    L = load_library()
+    need = int(L.fp8idx_workspace_bytes(OP_LOGITS_RAGGED, m, n, 1, 0))
+    wp, wb = _workspace(need, dev, workspace)
     with torch.cuda.device(dev):
-        st = load_library().indexer_logits_ragged(
+        st = L.indexer_logits_ragged(
             _ptr(q8), _ptr(kv8), _ptr(kv_scale), _ptr(weights), _ptr(ks), _ptr(ke), m, n, H, D,
-            _ptr(logits), logits.shape[1] if logits.dim() == 2 else n, int(bool(clean)), _stream(dev, stream))
+            _ptr(logits), logits.shape[1], int(bool(clean)), wp, wb, _stream(dev, stream))
     _check("indexer_logits_ragged", st)
     return logits
 
@@ -256,22 +396,16 @@ def indexer_logits_ragged(q, kv, kv_scale, weights, ks, ke, *, clean: bool = Tru
 def indexer_logits_paged(q, kv_pool, scale_pool, weights, row_len, block_table, *, width: int,
                          clean: bool = True, logits: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Paged-decode logits [B * next_n, width] float32."""
-    dev = _dev(q, "q")
-    q8 = _fp8(q, "q", dev)
-    pool8 = _fp8(kv_pool, "kv_pool", dev)
-    if q8.dim() != 4 or q8.shape[2:] != (H, D):
-        raise ValueError("q must be [B, next_n, 32, 128]")
-    B, nn = q8.shape[0], q8.shape[1]
-    if pool8.dim() != 3 or pool8.shape[2] != D:
-        raise ValueError("kv_pool must be [pages, page_size, 128]")
-    _need(scale_pool, "scale_pool", _F32, dev)
-    _need(weights, "weights", _F32, dev)
-    _need(row_len, "row_len", _I32T, dev)
-    _need(block_table, "block_table", _I32T, dev)
+    q8, pool8, B, nn = _paged_inputs(q, kv_pool, scale_pool, weights, row_len, block_table, width)
+    if logits is not None:
+        _need(logits, "logits", _F32)
+        if logits.dim() != 2 or logits.shape[0] != B * nn or logits.shape[1] < width:
+            raise ValueError(f"logits must be [{B * nn}, >= {width}] float32, got {tuple(logits.shape)}")
+    dev = _dev(q8, "q")
+    _same_device(dev, kv_pool=pool8, scale_pool=scale_pool, weights=weights, row_len=row_len,
+                 block_table=block_table, logits=logits)
     if logits is None:
         logits = torch.empty((B * nn, width), dtype=torch.float32, device=dev)
-    else:
-        _need(logits, "logits", _F32, dev)
     with torch.cuda.device(dev):
         st = load_library().indexer_logits_paged(
             _ptr(q8), _ptr(pool8), _ptr(scale_pool), _ptr(weights), _ptr(row_len), _ptr(block_table),
@@ -285,18 +419,25 @@ def indexer_topk(logits, ke, k: int, *, ks=None, width: Optional[int] = None, ro
                  map: Optional[TopkMap] = None, out: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Top-k [rows, k] int32 over logits [rows, ld] within [ks, ke)."""
-    dev = _dev(logits, "logits")
-    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1:
+    if not isinstance(logits, torch.Tensor) or logits.dtype != torch.float32 or logits.dim() != 2 \
+            or logits.stride(1) != 1:
         raise ValueError("logits must be a 2-D float32 tensor with unit column stride")
-    rows, ld = logits.shape[0], logits.stride(0) if logits.shape[0] > 1 else logits.shape[1]
+    rows = logits.shape[0]
+    ld = logits.stride(0) if rows > 1 else logits.shape[1]
     width = logits.shape[1] if width is None else int(width)
-    _need(ke, "ke", _I32T, dev)
+    if width < 0 or width > logits.shape[1]:
+        raise ValueError(f"width must lie in [0, {logits.shape[1]}] (the logits columns)")
+    _need(ke, "ke", _I32T)
+    _numel(ke, "ke", rows)
     if ks is not None:
-        _need(ks, "ks", _I32T, dev)
-    if out is None:
-        out = torch.empty((rows, k), dtype=torch.int32, device=dev)
-    else:
-        _need(out, "out", _I32T, dev)
+        _need(ks, "ks", _I32T)
+        _numel(ks, "ks", rows)
+    if map is not None:
+        map.check()
+    out = _out_rows(out, rows, k, logits.device)
+    dev = _dev(logits, "logits")
+    _same_device(dev, ke=ke, ks=ks, out=out, workspace=workspace)
+    _map_devices(map, dev)
     L = load_library()
     need = int(L.fp8idx_workspace_bytes(OP_TOPK, rows, width, k, 0))
     wp, wb = _workspace(need, dev, workspace)
@@ -312,20 +453,13 @@ def indexer_logits_topk_ragged(q, kv, kv_scale, weights, ks, ke, k: int, *,
                                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                                stream=None) -> torch.Tensor:
     """Fused ragged logits + top-k, row-chunked under ``logits_cap_bytes`` (0 = one chunk)."""
-    dev = _dev(q, "q")
-    q8 = _fp8(q, "q", dev)
-    kv8 = _fp8(kv, "kv", dev)
-    m, n = q8.shape[0], kv8.shape[0]
-    if q8.shape[1:] != (H, D) or kv8.shape[1:] != (D,):
-        raise ValueError("q must be [m, 32, 128] and kv [n, 128]")
-    _need(kv_scale, "kv_scale", _F32, dev)
-    _need(weights, "weights", _F32, dev)
-    _need(ks, "ks", _I32T, dev)
-    _need(ke, "ke", _I32T, dev)
-    if out is None:
-        out = torch.empty((m, k), dtype=torch.int32, device=dev)
-    else:
-        _need(out, "out", _I32T, dev)
+    q8, kv8, m, n = _ragged_inputs(q, kv, kv_scale, weights, ks, ke)
+    if map is not None:
+        map.check()
+    out = _out_rows(out, m, k, q8.device)
+    dev = _dev(q8, "q")
+    _same_device(dev, kv=kv8, kv_scale=kv_scale, weights=weights, ks=ks, ke=ke, out=out, workspace=workspace)
+    _map_devices(map, dev)
     L = load_library()
     need = int(L.fp8idx_workspace_bytes(OP_LOGITS_TOPK_RAGGED, m, n, k, logits_cap_bytes))
     wp, wb = _workspace(need, dev, workspace)
@@ -342,20 +476,13 @@ def indexer_logits_topk_ragged_overlap(q, kv, kv_scale, weights, ks, ke, k: int,
                                        out: Optional[torch.Tensor] = None,
                                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """indexer_logits_topk_ragged with chunk N - 1's top-k on ``side_stream`` while chunk N's logits run."""
-    dev = _dev(q, "q")
-    q8 = _fp8(q, "q", dev)
-    kv8 = _fp8(kv, "kv", dev)
-    m, n = q8.shape[0], kv8.shape[0]
-    if q8.shape[1:] != (H, D) or kv8.shape[1:] != (D,):
-        raise ValueError("q must be [m, 32, 128] and kv [n, 128]")
-    _need(kv_scale, "kv_scale", _F32, dev)
-    _need(weights, "weights", _F32, dev)
-    _need(ks, "ks", _I32T, dev)
-    _need(ke, "ke", _I32T, dev)
-    if out is None:
-        out = torch.empty((m, k), dtype=torch.int32, device=dev)
-    else:
-        _need(out, "out", _I32T, dev)
+    q8, kv8, m, n = _ragged_inputs(q, kv, kv_scale, weights, ks, ke)
+    if map is not None:
+        map.check()
+    out = _out_rows(out, m, k, q8.device)
+    dev = _dev(q8, "q")
+    _same_device(dev, kv=kv8, kv_scale=kv_scale, weights=weights, ks=ks, ke=ke, out=out, workspace=workspace)
+    _map_devices(map, dev)
     L = load_library()
     need = int(L.fp8idx_workspace_bytes(OP_LOGITS_TOPK_RAGGED_OVERLAP, m, n, k, logits_cap_bytes))
     wp, wb = _workspace(need, dev, workspace)
@@ -373,20 +500,11 @@ def indexer_logits_topk_paged(q, kv_pool, scale_pool, weights, row_len, block_ta
                               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                               stream=None) -> torch.Tensor:
     """Fused paged logits + top-k -> [B * next_n, k] int32 physical slots (or raw positions)."""
-    dev = _dev(q, "q")
-    q8 = _fp8(q, "q", dev)
-    pool8 = _fp8(kv_pool, "kv_pool", dev)
-    if q8.dim() != 4 or q8.shape[2:] != (H, D):
-        raise ValueError("q must be [B, next_n, 32, 128]")
-    B, nn = q8.shape[0], q8.shape[1]
-    _need(scale_pool, "scale_pool", _F32, dev)
-    _need(weights, "weights", _F32, dev)
-    _need(row_len, "row_len", _I32T, dev)
-    _need(block_table, "block_table", _I32T, dev)
-    if out is None:
-        out = torch.empty((B * nn, k), dtype=torch.int32, device=dev)
-    else:
-        _need(out, "out", _I32T, dev)
+    q8, pool8, B, nn = _paged_inputs(q, kv_pool, scale_pool, weights, row_len, block_table, width)
+    out = _out_rows(out, B * nn, k, q8.device)
+    dev = _dev(q8, "q")
+    _same_device(dev, kv_pool=pool8, scale_pool=scale_pool, weights=weights, row_len=row_len,
+                 block_table=block_table, out=out, workspace=workspace)
     L = load_library()
     need = int(L.fp8idx_workspace_bytes_paged(B, nn, width, k, logits_cap_bytes))
     wp, wb = _workspace(need, dev, workspace)
@@ -453,12 +571,16 @@ def indexer_prepare_ragged(seq_len, q_len, req_idx, table, *, max_q: int, max_ke
 
     ks/ke hold max_q entries and ragged_mem max_keys entries; entries past the totals are left as allocated.
     """
-    dev = _dev(seq_len, "seq_len")
     for t, n in ((seq_len, "seq_len"), (q_len, "q_len"), (req_idx, "req_idx"), (table, "table")):
-        _need(t, n, _I32T, dev)
+        _need(t, n, _I32T)
+    B = seq_len.numel()
+    _numel(seq_len, "seq_len", B)
+    _numel(q_len, "q_len", B)
+    _numel(req_idx, "req_idx", B)
     if table.dim() != 2:
         raise ValueError("table must be [rows, ld] int32")
-    B = seq_len.numel()
+    dev = _dev(seq_len, "seq_len")
+    _same_device(dev, q_len=q_len, req_idx=req_idx, table=table)
     out = {"cu_seq": torch.empty(B + 1, dtype=torch.int32, device=dev),
            "cu_q": torch.empty(B + 1, dtype=torch.int32, device=dev),
            "ks": torch.empty(max(max_q, 0), dtype=torch.int32, device=dev),
@@ -477,11 +599,18 @@ def indexer_prepare_ragged(seq_len, q_len, req_idx, table, *, max_q: int, max_ke
 def indexer_prepare_decode(seq_len, req_idx, req_to_page, next_n: int, *, max_pages: Optional[int] = None,
                            stream=None):
     """Paged decode / MTP index preparation -> (row_len [B * next_n], block_table [B, max_pages]) int32."""
-    dev = _dev(seq_len, "seq_len")
     for t, n in ((seq_len, "seq_len"), (req_idx, "req_idx"), (req_to_page, "req_to_page")):
-        _need(t, n, _I32T, dev)
+        _need(t, n, _I32T)
     B = seq_len.numel()
+    _numel(seq_len, "seq_len", B)
+    _numel(req_idx, "req_idx", B)
+    if req_to_page.dim() != 2:
+        raise ValueError("req_to_page must be [rows, ld] int32")
     mp = req_to_page.shape[1] if max_pages is None else int(max_pages)
+    if mp < 0 or mp > req_to_page.shape[1]:
+        raise ValueError(f"max_pages must lie in [0, {req_to_page.shape[1]}] (the req_to_page columns)")
+    dev = _dev(seq_len, "seq_len")
+    _same_device(dev, req_idx=req_idx, req_to_page=req_to_page)
     row_len = torch.empty(B * next_n, dtype=torch.int32, device=dev)
     bt = torch.empty((B, mp), dtype=torch.int32, device=dev)
     L = load_library()

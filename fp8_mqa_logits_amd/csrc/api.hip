@@ -7,7 +7,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 #include <cstring>
 #include <mutex>
 
@@ -82,7 +81,8 @@ fp8idx_status check_map(const fp8idx_map* map) {
       if (!aligned(map->table, 4) || (map->cu_rows && !aligned(map->cu_rows, 4))) return FP8IDX_EINVAL;
       return FP8IDX_OK;
     case FP8IDX_MAP_BLOCK_TABLE:
-      if (!map->table || map->ld < 1 || map->num_req < 1 || map->rows_per_req < 1 || map->page_size < 1)
+      if (!map->table || map->ld < 1 || map->num_req < 1 || map->rows_per_req < 1 || map->page_size < 1 ||
+          map->num_pages < 1)
         return FP8IDX_EINVAL;
       if (!aligned(map->table, 4)) return FP8IDX_EINVAL;
       return FP8IDX_OK;
@@ -104,6 +104,7 @@ fp8idx::TopkMap to_kernel_map(const fp8idx_map* map) {
   m.cu_rows = map->cu_rows;
   m.rows_per_req = map->rows_per_req;
   m.page_size = map->page_size;
+  m.num_pages = map->num_pages;
   return m;
 }
 
@@ -141,38 +142,161 @@ fp8idx_status check_topk_args(int32_t rows, int32_t width, int64_t ld, int32_t k
   return FP8IDX_OK;
 }
 
-// Events of the overlapped fused entry, created once per device: [0..1] a
-// chunk buffer's logits are written, [2..3] its top-k has read them.
-std::once_flag g_ev_once[kMaxDevices];
-hipEvent_t g_ev[kMaxDevices][4];
-int g_ev_ok[kMaxDevices];
-
-fp8idx_status overlap_events(hipEvent_t** out) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8IDX_EDEVICE;
-  std::call_once(g_ev_once[dev], [dev]() {
-    g_ev_ok[dev] = 1;
-    for (int i = 0; i < 4; ++i)
-      if (hipEventCreateWithFlags(&g_ev[dev][i], hipEventDisableTiming) != hipSuccess) g_ev_ok[dev] = 0;
-  });
-  if (!g_ev_ok[dev]) return FP8IDX_EHIP;
-  *out = g_ev[dev];
+fp8idx_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return FP8IDX_OK;
+  if (ws == nullptr || ws_bytes < need) return FP8IDX_EWORKSPACE;
+  if (!aligned(ws, 256)) return FP8IDX_EINVAL;
   return FP8IDX_OK;
 }
 
-size_t fused_ws_bytes(int32_t rows, int64_t width, int32_t k, size_t cap, int32_t granule,
-                      int32_t logit_buffers = 1) {
+// Layout of the fused entries' workspace: [queue counters (ragged only)] [chunk logits x buffers]
+// [top-k candidates].  ok is false when the arguments are rejected (an unsupported top-k plan).
+struct FusedLayout {
+  bool ok;
+  int32_t rpc;          // rows per chunk
+  size_t queue_bytes;   // work-queue counters of the ragged logits launches
+  size_t buf_bytes;     // one chunk of logits
+  int32_t buffers;      // chunk logits buffers (2 when the overlap entry alternates them)
+  size_t topk_bytes;    // candidates of the largest chunk's top-k
+  size_t total;
+};
+
+FusedLayout fused_layout(int32_t rows, int64_t width, int32_t k, size_t cap, int32_t granule, bool ragged,
+                         int32_t logit_buffers = 1) {
+  FusedLayout L{};
   const int64_t ld = ws_logits_ld(width);
   int32_t rpc = rows_per_chunk(cap, ld, rows);
   if (granule > 1 && rpc < rows) rpc = std::max<int32_t>(granule, rpc / granule * granule);
   rpc = std::min(rpc, rows);
-  if (rpc <= 0) return 0;
+  if (rpc <= 0) return L;
   const int32_t last = rows % rpc == 0 ? rpc : rows % rpc;
-  const size_t logits = align256((size_t)rpc * (size_t)ld * 4u) * (size_t)(rpc < rows ? logit_buffers : 1);
-  const size_t t0 = fp8idx::topk_workspace_bytes(fp8idx::plan_topk(rpc, width, k));
-  const size_t t1 = fp8idx::topk_workspace_bytes(fp8idx::plan_topk(last, width, k));
-  return logits + std::max(t0, t1);
+  const fp8idx::TopkPlan p0 = fp8idx::plan_topk(rpc, width, k);
+  const fp8idx::TopkPlan p1 = fp8idx::plan_topk(last, width, k);
+  if (!p0.supported || !p1.supported) return L;
+  L.ok = true;
+  L.rpc = rpc;
+  L.queue_bytes = ragged ? fp8idx::kRaggedQueueBytes : 0;
+  L.buf_bytes = align256((size_t)rpc * (size_t)ld * 4u);
+  L.buffers = rpc < rows ? logit_buffers : 1;
+  L.topk_bytes = std::max(fp8idx::topk_workspace_bytes(p0), fp8idx::topk_workspace_bytes(p1));
+  L.total = L.queue_bytes + L.buf_bytes * (size_t)L.buffers + L.topk_bytes;
+  return L;
 }
+
+// ---- argument validation, shared by the entry points and fp8idx_validate_only ----------------
+
+fp8idx_status validate_logits_ragged(const fp8idx_call_args& c) {
+  if (fp8idx_status s = check_ragged(c.q, c.kv, c.kv_scale, c.weights, c.ks, c.ke, c.m, c.n, c.H, c.D)) return s;
+  if (c.m == 0) return FP8IDX_OK;
+  if (!c.logits || !aligned(c.logits, 4) || c.ld_logits < c.n) return FP8IDX_EINVAL;
+  return check_ws(c.ws, c.ws_bytes, fp8idx::kRaggedQueueBytes);
+}
+
+fp8idx_status validate_logits_paged(const fp8idx_call_args& c) {
+  if (fp8idx_status s = check_paged(c.q, c.kv, c.kv_scale, c.weights, c.row_len, c.block_table, c.B, c.next_n,
+                                    c.H, c.D, c.page_size, c.max_pages, c.num_pages, c.width))
+    return s;
+  if (c.B > 0 && (!c.logits || !aligned(c.logits, 4) || c.ld_logits < c.width || c.ld_logits < 1))
+    return FP8IDX_EINVAL;
+  return FP8IDX_OK;
+}
+
+fp8idx_status validate_topk(const fp8idx_call_args& c) {
+  if (fp8idx_status s = check_topk_args(c.rows, c.width, c.ld_logits, c.k, c.ld_out)) return s;
+  if (fp8idx_status s = check_map(c.map)) return s;
+  if (c.rows == 0) return FP8IDX_OK;
+  if (!c.scores || !c.ke || !c.out || c.row0 < 0) return FP8IDX_EINVAL;
+  if (!aligned(c.scores, 4) || !aligned(c.ke, 4) || !aligned(c.out, 4) || (c.ks && !aligned(c.ks, 4)))
+    return FP8IDX_EINVAL;
+  const fp8idx::TopkPlan plan = fp8idx::plan_topk(c.rows, c.width, c.k);
+  if (!plan.supported) return FP8IDX_EUNSUPPORTED;
+  return check_ws(c.ws, c.ws_bytes, fp8idx::topk_workspace_bytes(plan));
+}
+
+fp8idx_status validate_fused_ragged(const fp8idx_call_args& c, bool overlap) {
+  if (fp8idx_status s = check_ragged(c.q, c.kv, c.kv_scale, c.weights, c.ks, c.ke, c.m, c.n, c.H, c.D)) return s;
+  if (fp8idx_status s = check_topk_args(c.m, c.n, c.n, c.k, c.ld_out)) return s;
+  if (fp8idx_status s = check_map(c.map)) return s;
+  if (c.m == 0) return FP8IDX_OK;
+  if (!c.out || !aligned(c.out, 4)) return FP8IDX_EINVAL;
+  if (overlap && (c.side_stream == nullptr || c.side_stream == c.stream)) return FP8IDX_EINVAL;
+  const FusedLayout L = fused_layout(c.m, c.n, c.k, c.logits_cap_bytes, 1, true, overlap ? 2 : 1);
+  if (!L.ok) return FP8IDX_EUNSUPPORTED;
+  return check_ws(c.ws, c.ws_bytes, L.total);
+}
+
+fp8idx_status validate_fused_paged(const fp8idx_call_args& c) {
+  if (fp8idx_status s = check_paged(c.q, c.kv, c.kv_scale, c.weights, c.row_len, c.block_table, c.B, c.next_n,
+                                    c.H, c.D, c.page_size, c.max_pages, c.num_pages, c.width))
+    return s;
+  const int32_t rows = (int32_t)((int64_t)c.B * c.next_n);
+  if (fp8idx_status s = check_topk_args(rows, c.width, std::max<int64_t>(c.width, 1), c.k, c.ld_out)) return s;
+  if (rows == 0) return FP8IDX_OK;
+  if (!c.out || !aligned(c.out, 4)) return FP8IDX_EINVAL;
+  const FusedLayout L = fused_layout(rows, c.width, c.k, c.logits_cap_bytes, c.next_n, false);
+  if (!L.ok) return FP8IDX_EUNSUPPORTED;
+  return check_ws(c.ws, c.ws_bytes, L.total);
+}
+
+fp8idx_call_args ragged_call(const uint8_t* q, const uint8_t* kv, const float* kv_scale, const float* weights,
+                             const int32_t* ks, const int32_t* ke, int32_t m, int32_t n, int32_t H, int32_t D) {
+  fp8idx_call_args c{};
+  c.q = q;
+  c.kv = kv;
+  c.kv_scale = kv_scale;
+  c.weights = weights;
+  c.ks = ks;
+  c.ke = ke;
+  c.m = m;
+  c.n = n;
+  c.H = H;
+  c.D = D;
+  return c;
+}
+
+fp8idx_call_args paged_call(const uint8_t* q, const uint8_t* kv_pool, const float* scale_pool,
+                            const float* weights, const int32_t* row_len, const int32_t* block_table, int32_t B,
+                            int32_t next_n, int32_t H, int32_t D, int32_t page_size, int32_t max_pages,
+                            int64_t num_pages, int32_t width) {
+  fp8idx_call_args c{};
+  c.q = q;
+  c.kv = kv_pool;
+  c.kv_scale = scale_pool;
+  c.weights = weights;
+  c.row_len = row_len;
+  c.block_table = block_table;
+  c.B = B;
+  c.next_n = next_n;
+  c.H = H;
+  c.D = D;
+  c.page_size = page_size;
+  c.max_pages = max_pages;
+  c.num_pages = num_pages;
+  c.width = width;
+  return c;
+}
+
+// The four ordering events of one overlapped call, created for the call and destroyed at its end.
+// A wait enqueued on a stream keeps the event state at the time it was enqueued, and destroying an
+// event whose recorded work is still pending is allowed (its resources go once that work ends), so
+// nothing here outlives the call.
+struct CallEvents {
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+  hipError_t create() {
+    for (auto& e : ev) {
+      const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+      if (r != hipSuccess) {
+        e = nullptr;
+        return r;
+      }
+    }
+    return hipSuccess;
+  }
+  ~CallEvents() {
+    for (auto& e : ev)
+      if (e) (void)hipEventDestroy(e);
+  }
+};
 
 }  // namespace
 
@@ -226,16 +350,32 @@ fp8idx_status indexer_sparse_mla(const uint16_t* q, const uint8_t* kv, const flo
 }
 
 size_t fp8idx_workspace_bytes(int32_t op, int32_t rows, int64_t width, int32_t k, size_t logits_cap_bytes) {
+  if (op == FP8IDX_OP_LOGITS_RAGGED) return rows > 0 && width > 0 ? fp8idx::kRaggedQueueBytes : 0;
   if (rows <= 0 || width < 0 || k < 1 || k > fp8idx::kMaxK) return 0;
   switch (op) {
-    case FP8IDX_OP_TOPK:
-      return fp8idx::topk_workspace_bytes(fp8idx::plan_topk(rows, width, k));
+    case FP8IDX_OP_TOPK: {
+      const fp8idx::TopkPlan p = fp8idx::plan_topk(rows, width, k);
+      return p.supported ? fp8idx::topk_workspace_bytes(p) : 0;
+    }
     case FP8IDX_OP_LOGITS_TOPK_RAGGED:
-      return fused_ws_bytes(rows, width, k, logits_cap_bytes, 1);
+      return fused_layout(rows, width, k, logits_cap_bytes, 1, true).total;
     case FP8IDX_OP_LOGITS_TOPK_RAGGED_OVERLAP:
-      return fused_ws_bytes(rows, width, k, logits_cap_bytes, 1, 2);
+      return fused_layout(rows, width, k, logits_cap_bytes, 1, true, 2).total;
     default:
       return 0;
+  }
+}
+
+fp8idx_status fp8idx_validate_only(int32_t entry, const fp8idx_call_args* args) {
+  if (args == nullptr) return FP8IDX_EINVAL;
+  switch (entry) {
+    case FP8IDX_ENTRY_LOGITS_RAGGED: return validate_logits_ragged(*args);
+    case FP8IDX_ENTRY_LOGITS_PAGED: return validate_logits_paged(*args);
+    case FP8IDX_ENTRY_TOPK: return validate_topk(*args);
+    case FP8IDX_ENTRY_LOGITS_TOPK_RAGGED: return validate_fused_ragged(*args, false);
+    case FP8IDX_ENTRY_LOGITS_TOPK_RAGGED_OVERLAP: return validate_fused_ragged(*args, true);
+    case FP8IDX_ENTRY_LOGITS_TOPK_PAGED: return validate_fused_paged(*args);
+    default: return FP8IDX_EINVAL;
   }
 }
 
@@ -307,13 +447,20 @@ fp8idx_status indexer_quant_fp8(const float* x, int64_t ld_x, int64_t rows, int3
 fp8idx_status indexer_logits_ragged(const uint8_t* q, const uint8_t* kv, const float* kv_scale,
                                     const float* weights, const int32_t* ks, const int32_t* ke,
                                     int32_t m, int32_t n, int32_t H, int32_t D,
-                                    float* logits, int64_t ld_logits, int32_t clean, void* stream) {
-  if (fp8idx_status s = check_ragged(q, kv, kv_scale, weights, ks, ke, m, n, H, D)) return s;
-  if (m > 0 && (!logits || !aligned(logits, 4) || ld_logits < n)) return FP8IDX_EINVAL;
+                                    float* logits, int64_t ld_logits, int32_t clean, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  fp8idx_call_args c = ragged_call(q, kv, kv_scale, weights, ks, ke, m, n, H, D);
+  c.logits = logits;
+  c.ld_logits = ld_logits;
+  c.clean = clean;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  if (fp8idx_status s = validate_logits_ragged(c)) return s;
   if (m == 0) return FP8IDX_OK;
   DeviceInfo dev;
   if (fp8idx_status s = current_device(&dev)) return s;
-  fp8idx::RaggedLogitsArgs a{q, kv, kv_scale, weights, ks, ke, m, n, logits, ld_logits, clean};
+  fp8idx::RaggedLogitsArgs a{q, kv, kv_scale, weights, ks, ke, m, n, logits, ld_logits, clean,
+                             static_cast<unsigned int*>(ws)};
   const hipError_t e = fp8idx::launch_logits_ragged(a, dev, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8IDX_OK : hip_fail(e);
 }
@@ -323,10 +470,12 @@ fp8idx_status indexer_logits_paged(const uint8_t* q, const uint8_t* kv_pool, con
                                    int32_t B, int32_t next_n, int32_t H, int32_t D, int32_t page_size,
                                    int32_t max_pages, int64_t num_pages, float* logits, int64_t ld_logits,
                                    int32_t width, int32_t clean, void* stream) {
-  if (fp8idx_status s = check_paged(q, kv_pool, scale_pool, weights, row_len, block_table, B, next_n, H, D,
-                                    page_size, max_pages, num_pages, width))
-    return s;
-  if (B > 0 && (!logits || !aligned(logits, 4) || ld_logits < width || ld_logits < 1)) return FP8IDX_EINVAL;
+  fp8idx_call_args c = paged_call(q, kv_pool, scale_pool, weights, row_len, block_table, B, next_n, H, D,
+                                  page_size, max_pages, num_pages, width);
+  c.logits = logits;
+  c.ld_logits = ld_logits;
+  c.clean = clean;
+  if (fp8idx_status s = validate_logits_paged(c)) return s;
   if (B == 0 || width == 0) return FP8IDX_OK;
   DeviceInfo dev;
   if (fp8idx_status s = current_device(&dev)) return s;
@@ -339,17 +488,25 @@ fp8idx_status indexer_logits_paged(const uint8_t* q, const uint8_t* kv_pool, con
 fp8idx_status indexer_topk(const float* logits, int64_t ld, int32_t rows, int32_t width, const int32_t* ks,
                            const int32_t* ke, int32_t k, int32_t row0, const fp8idx_map* map, int32_t* out,
                            int64_t ld_out, void* ws, size_t ws_bytes, void* stream) {
-  if (fp8idx_status s = check_topk_args(rows, width, ld, k, ld_out)) return s;
-  if (fp8idx_status s = check_map(map)) return s;
+  fp8idx_call_args c{};
+  c.scores = logits;
+  c.ld_logits = ld;
+  c.rows = rows;
+  c.width = width;
+  c.ks = ks;
+  c.ke = ke;
+  c.k = k;
+  c.row0 = row0;
+  c.map = map;
+  c.out = out;
+  c.ld_out = ld_out;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  if (fp8idx_status s = validate_topk(c)) return s;
   if (rows == 0) return FP8IDX_OK;
-  if (!logits || !ke || !out || row0 < 0) return FP8IDX_EINVAL;
-  if (!aligned(logits, 4) || !aligned(ke, 4) || !aligned(out, 4) || (ks && !aligned(ks, 4))) return FP8IDX_EINVAL;
-  const fp8idx::TopkPlan plan = fp8idx::plan_topk(rows, width, k);
-  const size_t need = fp8idx::topk_workspace_bytes(plan);
-  if (need > 0 && (ws == nullptr || ws_bytes < need)) return FP8IDX_EWORKSPACE;
-  if (need > 0 && !aligned(ws, 256)) return FP8IDX_EINVAL;
   DeviceInfo dev;
   if (fp8idx_status s = current_device(&dev)) return s;
+  const fp8idx::TopkPlan plan = fp8idx::plan_topk(rows, width, k);
   fp8idx::TopkArgs a{logits, ld, rows, width, ks, ke, k, row0, to_kernel_map(map), out, ld_out};
   const hipError_t e = fp8idx::launch_topk(a, plan, ws, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8IDX_OK : hip_fail(e);
@@ -360,27 +517,32 @@ fp8idx_status indexer_logits_topk_ragged(const uint8_t* q, const uint8_t* kv, co
                                          int32_t n, int32_t H, int32_t D, int32_t k, const fp8idx_map* map,
                                          int32_t* out, int64_t ld_out, size_t logits_cap_bytes, void* ws,
                                          size_t ws_bytes, void* stream) {
-  if (fp8idx_status s = check_ragged(q, kv, kv_scale, weights, ks, ke, m, n, H, D)) return s;
-  if (fp8idx_status s = check_topk_args(m, n, n, k, ld_out)) return s;
-  if (fp8idx_status s = check_map(map)) return s;
+  fp8idx_call_args c = ragged_call(q, kv, kv_scale, weights, ks, ke, m, n, H, D);
+  c.k = k;
+  c.map = map;
+  c.out = out;
+  c.ld_out = ld_out;
+  c.logits_cap_bytes = logits_cap_bytes;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  if (fp8idx_status s = validate_fused_ragged(c, false)) return s;
   if (m == 0) return FP8IDX_OK;
-  if (!out || !aligned(out, 4)) return FP8IDX_EINVAL;
-  const size_t need = fused_ws_bytes(m, n, k, logits_cap_bytes, 1);
-  if (ws == nullptr || ws_bytes < need) return FP8IDX_EWORKSPACE;
-  if (!aligned(ws, 256)) return FP8IDX_EINVAL;
   DeviceInfo dev;
   if (fp8idx_status s = current_device(&dev)) return s;
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  const FusedLayout L = fused_layout(m, n, k, logits_cap_bytes, 1, true);
   const int64_t ld = ws_logits_ld(n);
-  const int32_t rpc = rows_per_chunk(logits_cap_bytes, ld, m);
-  float* chunk_logits = static_cast<float*>(ws);
-  void* topk_ws = static_cast<uint8_t*>(ws) + align256((size_t)rpc * (size_t)ld * 4u);
+  const int32_t rpc = L.rpc;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  unsigned int* queue = reinterpret_cast<unsigned int*>(w);
+  float* chunk_logits = reinterpret_cast<float*>(w + L.queue_bytes);
+  void* topk_ws = w + L.queue_bytes + L.buf_bytes;
   const fp8idx::TopkMap kmap = to_kernel_map(map);
   for (int32_t s0 = 0; s0 < m; s0 += rpc) {
     const int32_t rows = std::min(rpc, m - s0);
     fp8idx::RaggedLogitsArgs la{q + (size_t)s0 * fp8idx::kQRowBytesHost, kv, kv_scale,
-                                weights + (size_t)s0 * 32, ks + s0, ke + s0, rows, n, chunk_logits, ld, 0};
+                                weights + (size_t)s0 * 32, ks + s0, ke + s0, rows, n, chunk_logits, ld, 0, queue};
     hipError_t e = fp8idx::launch_logits_ragged(la, dev, st);
     if (e != hipSuccess) return hip_fail(e);
     const fp8idx::TopkPlan plan = fp8idx::plan_topk(rows, n, k);
@@ -397,39 +559,46 @@ fp8idx_status indexer_logits_topk_ragged_overlap(const uint8_t* q, const uint8_t
                                                  const fp8idx_map* map, int32_t* out, int64_t ld_out,
                                                  size_t logits_cap_bytes, void* ws, size_t ws_bytes, void* stream,
                                                  void* side_stream) {
-  if (fp8idx_status s = check_ragged(q, kv, kv_scale, weights, ks, ke, m, n, H, D)) return s;
-  if (fp8idx_status s = check_topk_args(m, n, n, k, ld_out)) return s;
-  if (fp8idx_status s = check_map(map)) return s;
+  fp8idx_call_args c = ragged_call(q, kv, kv_scale, weights, ks, ke, m, n, H, D);
+  c.k = k;
+  c.map = map;
+  c.out = out;
+  c.ld_out = ld_out;
+  c.logits_cap_bytes = logits_cap_bytes;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  c.stream = stream;
+  c.side_stream = side_stream;
+  if (fp8idx_status s = validate_fused_ragged(c, true)) return s;
   if (m == 0) return FP8IDX_OK;
-  if (!out || !aligned(out, 4)) return FP8IDX_EINVAL;
-  if (side_stream == nullptr || side_stream == stream) return FP8IDX_EINVAL;
-  const size_t need = fused_ws_bytes(m, n, k, logits_cap_bytes, 1, 2);
-  if (ws == nullptr || ws_bytes < need) return FP8IDX_EWORKSPACE;
-  if (!aligned(ws, 256)) return FP8IDX_EINVAL;
   DeviceInfo dev;
   if (fp8idx_status s = current_device(&dev)) return s;
-  hipEvent_t* ev = nullptr;
-  if (fp8idx_status s = overlap_events(&ev)) return s;
+  CallEvents events;
+  if (hipError_t e = events.create()) return hip_fail(e);
+  hipEvent_t* ev = events.ev;
 
   const hipStream_t main_st = static_cast<hipStream_t>(stream);
   const hipStream_t side = static_cast<hipStream_t>(side_stream);
+  const FusedLayout L = fused_layout(m, n, k, logits_cap_bytes, 1, true, 2);
   const int64_t ld = ws_logits_ld(n);
-  const int32_t rpc = rows_per_chunk(logits_cap_bytes, ld, m);
+  const int32_t rpc = L.rpc;
   const int32_t nchunks = (m + rpc - 1) / rpc;
-  const size_t buf_bytes = align256((size_t)rpc * (size_t)ld * 4u);
-  float* bufs[2] = {static_cast<float*>(ws),
-                    reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + (nchunks > 1 ? buf_bytes : 0))};
-  void* topk_ws = static_cast<uint8_t*>(ws) + buf_bytes * (nchunks > 1 ? 2 : 1);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  unsigned int* queue = reinterpret_cast<unsigned int*>(w);
+  float* bufs[2] = {reinterpret_cast<float*>(w + L.queue_bytes),
+                    reinterpret_cast<float*>(w + L.queue_bytes + (L.buffers > 1 ? L.buf_bytes : 0))};
+  void* topk_ws = w + L.queue_bytes + L.buf_bytes * (size_t)L.buffers;
   const fp8idx::TopkMap kmap = to_kernel_map(map);
   hipError_t e = hipSuccess;
-  for (int32_t c = 0; c < nchunks; ++c) {
-    const int32_t s0 = c * rpc;
+  for (int32_t ci = 0; ci < nchunks; ++ci) {
+    const int32_t s0 = ci * rpc;
     const int32_t rows = std::min(rpc, m - s0);
-    const int b = c & 1;
-    // the top-k of chunk c - 2 must have read this buffer before it is rewritten
-    if (c >= 2 && (e = hipStreamWaitEvent(main_st, ev[2 + b], 0)) != hipSuccess) return hip_fail(e);
+    const int b = ci & 1;
+    // the top-k of chunk ci - 2 must have read this buffer before it is rewritten
+    if (ci >= 2 && (e = hipStreamWaitEvent(main_st, ev[2 + b], 0)) != hipSuccess) return hip_fail(e);
+    // the logits launches all run on the main stream, one after another, so they share one counter set
     fp8idx::RaggedLogitsArgs la{q + (size_t)s0 * fp8idx::kQRowBytesHost, kv, kv_scale,
-                                weights + (size_t)s0 * 32, ks + s0, ke + s0, rows, n, bufs[b], ld, 0};
+                                weights + (size_t)s0 * 32, ks + s0, ke + s0, rows, n, bufs[b], ld, 0, queue};
     if ((e = fp8idx::launch_logits_ragged(la, dev, main_st)) != hipSuccess) return hip_fail(e);
     if ((e = hipEventRecord(ev[b], main_st)) != hipSuccess) return hip_fail(e);
     if ((e = hipStreamWaitEvent(side, ev[b], 0)) != hipSuccess) return hip_fail(e);
@@ -449,28 +618,28 @@ fp8idx_status indexer_logits_topk_paged(const uint8_t* q, const uint8_t* kv_pool
                                         int32_t max_pages, int64_t num_pages, int32_t width, int32_t k,
                                         int32_t map_to_slots, int32_t* out, int64_t ld_out,
                                         size_t logits_cap_bytes, void* ws, size_t ws_bytes, void* stream) {
-  if (fp8idx_status s = check_paged(q, kv_pool, scale_pool, weights, row_len, block_table, B, next_n, H, D,
-                                    page_size, max_pages, num_pages, width))
-    return s;
-  const int64_t rows64 = (int64_t)B * next_n;
-  const int32_t rows = (int32_t)rows64;
-  if (fp8idx_status s = check_topk_args(rows, width, std::max<int64_t>(width, 1), k, ld_out)) return s;
+  fp8idx_call_args c = paged_call(q, kv_pool, scale_pool, weights, row_len, block_table, B, next_n, H, D,
+                                  page_size, max_pages, num_pages, width);
+  c.k = k;
+  c.map_to_slots = map_to_slots;
+  c.out = out;
+  c.ld_out = ld_out;
+  c.logits_cap_bytes = logits_cap_bytes;
+  c.ws = ws;
+  c.ws_bytes = ws_bytes;
+  if (fp8idx_status s = validate_fused_paged(c)) return s;
+  const int32_t rows = (int32_t)((int64_t)B * next_n);
   if (rows == 0) return FP8IDX_OK;
-  if (!out || !aligned(out, 4)) return FP8IDX_EINVAL;
-  const size_t need = fused_ws_bytes(rows, width, k, logits_cap_bytes, next_n);
-  if (ws == nullptr || ws_bytes < need) return FP8IDX_EWORKSPACE;
-  if (!aligned(ws, 256)) return FP8IDX_EINVAL;
   DeviceInfo dev;
   if (fp8idx_status s = current_device(&dev)) return s;
 
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  const FusedLayout L = fused_layout(rows, width, k, logits_cap_bytes, next_n, false);
   const int64_t ld = ws_logits_ld(width);
-  int32_t rpc = rows_per_chunk(logits_cap_bytes, ld, rows);
-  if (rpc < rows) rpc = std::max<int32_t>(next_n, rpc / next_n * next_n);
-  rpc = std::min(rpc, rows);
+  const int32_t rpc = L.rpc;
   const int32_t req_per_chunk = std::max<int32_t>(1, rpc / next_n);
   float* chunk_logits = static_cast<float*>(ws);
-  void* topk_ws = static_cast<uint8_t*>(ws) + align256((size_t)rpc * (size_t)ld * 4u);
+  void* topk_ws = static_cast<uint8_t*>(ws) + L.buf_bytes;
   fp8idx::TopkMap kmap{};
   if (map_to_slots) {
     kmap.kind = FP8IDX_MAP_BLOCK_TABLE;
@@ -479,6 +648,7 @@ fp8idx_status indexer_logits_topk_paged(const uint8_t* q, const uint8_t* kv_pool
     kmap.num_req = B;
     kmap.rows_per_req = next_n;
     kmap.page_size = page_size;
+    kmap.num_pages = num_pages;
   } else {
     kmap.kind = FP8IDX_MAP_NONE;
   }
@@ -502,7 +672,7 @@ fp8idx_status indexer_logits_topk_paged(const uint8_t* q, const uint8_t* kv_pool
 
 size_t fp8idx_workspace_bytes_paged(int32_t B, int32_t next_n, int32_t width, int32_t k, size_t logits_cap_bytes) {
   if (B <= 0 || next_n <= 0 || width < 0 || k < 1 || k > fp8idx::kMaxK) return 0;
-  return fused_ws_bytes(B * next_n, width, k, logits_cap_bytes, next_n);
+  return fused_layout(B * next_n, width, k, logits_cap_bytes, next_n, false).total;
 }
 
 }  // extern "C"

@@ -19,7 +19,13 @@ struct RaggedLogitsArgs {
   float* logits;
   int64_t ld;
   int32_t clean;
+  unsigned int* queue;   // kRaggedQueueWords work-queue counters (device), cleared by each launch
 };
+
+// Work-queue counters of one ragged logits launch: one claim counter per XCD queue, padded to
+// 256 bytes so that the counters of a workspace never share a cache line with other data.
+constexpr int kRaggedQueueWords = 8;
+constexpr size_t kRaggedQueueBytes = 256;
 
 struct PagedLogitsArgs {
   const uint8_t* q;
@@ -46,6 +52,7 @@ struct TopkMap {
   const int32_t* cu_rows;
   int32_t rows_per_req;
   int32_t page_size;
+  int64_t num_pages;   // block table: page ids outside [0, num_pages) map to -1
 };
 
 struct TopkArgs {
@@ -78,6 +85,7 @@ constexpr int kMaxK = 16384;
 
 struct TopkPlan {
   int nlevels;
+  bool supported;       // false: the merge would need more than kMaxTopkLevels levels
   TopkLevel level[kMaxTopkLevels];
   size_t buf_bytes[2];  // ping-pong candidate buffers (bytes each)
 };

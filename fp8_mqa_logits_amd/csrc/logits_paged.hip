@@ -26,7 +26,8 @@
 // - Scoring, ReLU, head weighting and the cross-lane head reduction are the
 //   same register-resident core as the ragged kernel.
 // - With clean set, keys past a unit's scored range are filled with -inf by a
-//   second balanced split over (unit, 64-key block) pairs.
+//   second balanced split over (unit, 64-key block) pairs.  Keys inside a
+//   row's window whose page id lies outside the pool get -inf in any case.
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -213,7 +214,9 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
     claim();   // the next chunk's page ids load while this chunk is scored
 
     // Scores chunk page i from pf; a step past the chunk's end (live false)
-    // computes on page 0's data and stores nothing.
+    // computes on page 0's data and stores nothing.  Keys of the row's window
+    // on a page id outside the pool hold no kv: they get -inf (whatever
+    // `clean` says), so a top-k over the window never reads a stale value.
     auto score_page = [&](int i, const PageFrags& pf) {
       const bool live = i < cur_n;
       const int32_t pid = __builtin_amdgcn_readlane(cur_pidv, i);
@@ -227,8 +230,8 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
 #pragma unroll
       for (int f = 0; f < kFragsPerPage; ++f) {
         const int j = (cur_pg + i) * kPage + f * 16 + (lane & 15);
-        const bool val = ok && j < my_len;
-        if (live && row_ok && j < covered && (val || clean)) out_row[j] = val ? v[f] : -INFINITY;
+        const bool inwin = j < my_len;
+        if (live && row_ok && j < covered && (inwin || clean)) out_row[j] = ok && inwin ? v[f] : -INFINITY;
       }
     };
     // One page loads while the previous one is scored; the chunk's last step

@@ -10,15 +10,25 @@
 //   of the keys); each wave of a workgroup owns 4 of the item's rows, whose
 //   q (4 rows x 32 heads x 128 bytes) stays in VGPRs as eight 16x16x128 MFMA
 //   A-operands next to the matching weights.
-// - The grid holds only as many workgroups as are resident at once.  The
-//   items' 64-key tiles, laid end to end in split-major order, are divided
-//   into equal contiguous ranges, one per workgroup, which each workgroup
-//   finds by itself from ks/ke (a prefix scan over the row blocks' windows),
-//   so no host schedule or workspace is needed.  Windows that differ between
-//   rows (the causal triangle) therefore do not leave some workgroups with
-//   more tiles than others.  Workgroups are dealt to the 8 XCDs round-robin;
-//   ranks are assigned XCD-major, so each XCD covers one contiguous eighth of
-//   the order, about one kv slice, which stays in its L2.
+// - The grid is persistent: as many workgroups as are resident at once.  The
+//   items sit in 8 queues, one per XCD: queue x holds the key slices x, x + 8,
+//   x + 16, ... of every row block, row blocks from the last (the longest
+//   causal windows) to the first.  Workgroups are dealt to the XCDs
+//   round-robin, so queue blockIdx % 8 is served by one XCD and its kv slices
+//   stay in that XCD's L2.  A workgroup's first item is fixed (item
+//   blockIdx / 8 of its queue); after that it claims items with one atomic
+//   per item on its queue's counter, and once that queue is empty it moves to
+//   another queue that still has items.  Co-resident workgroups are not
+//   served at equal rates (issue favours older waves), so dynamic claims
+//   balance the finish times where any static split leaves the slowest
+//   workgroup of each CU last.
+// - The counters (8 words) live in a buffer that the caller's workspace
+//   brings in, one per launch.  The launcher clears them with a one-wave
+//   kernel on the same stream right before the logits kernel, so a launch
+//   never depends on what an earlier one left there; when the fixed first
+//   items cover every queue (small problems) neither the clear nor any
+//   atomic runs.  Two launches that may run at the same time must therefore
+//   be given different counter buffers.
 // - Keys stream through LDS in tiles of 64 keys x 128 bytes (8 KiB, double
 //   buffered), loaded with coalesced 16-byte global loads.  Inside a row the
 //   16-byte chunks are XOR-swizzled by (key & 7) so that the B-operand reads
@@ -40,17 +50,12 @@
 #include "mqa_core.hpp"
 
 #include <algorithm>
-#include <mutex>
 
 namespace fp8idx {
 
 constexpr int kTileKeys = 64;
-constexpr int kQueueSlots = 64;   // streams with a slot of their own
-
-// Work-queue counters: per slot, one claim counter per XCD queue and a count of finished
-// workgroups.  The last workgroup of a launch resets its slot, so the next launch on the slot
-// starts from zero.  Slots belong to streams: launches on one stream never overlap.
-__device__ unsigned int g_ragged_queue[kQueueSlots][16];
+constexpr int kWaves = 4;
+constexpr int kRowsPerItem = 4 * kWaves;
 
 // Tiles of one item: row block with key window union [lo, hi), split [split_lo, split_hi).
 struct ItemGeom {
@@ -74,27 +79,38 @@ constexpr unsigned int kNoItem = 0xffffffffu;
 __device__ __forceinline__ int queue_splits(int splits, int x) { return splits > x ? (splits - x + 7) / 8 : 0; }
 
 // Workgroups whose fixed first item comes from queue x (those with blockIdx % 8 == x).
-__device__ __forceinline__ unsigned int queue_fixed(int x) { return (gridDim.x + 7u - (unsigned int)x) / 8u; }
+__host__ __device__ __forceinline__ unsigned int queue_fixed(unsigned int grid, int x) {
+  return (grid + 7u - (unsigned int)x) / 8u;
+}
 
 // Items of queue x.
-__device__ __forceinline__ unsigned int queue_items(int splits, int row_blocks, int x) {
-  return (unsigned int)(queue_splits(splits, x) * row_blocks);
+__host__ __device__ __forceinline__ unsigned int queue_items(int splits, int row_blocks, int x) {
+  return (unsigned int)((splits > x ? (splits - x + 7) / 8 : 0) * row_blocks);
+}
+
+// True when the fixed first items (one per workgroup) leave some queue with items to claim.
+__host__ __device__ __forceinline__ bool queues_needed(unsigned int grid, int splits, int row_blocks) {
+  bool need = false;
+  for (int x = 0; x < 8; ++x) need = need || queue_items(splits, row_blocks, x) > queue_fixed(grid, x);
+  return need;
 }
 
 // Next item of a workgroup as (index in queue) * 8 + queue, or kNoItem once every queue is empty.
 // `state` (thread 0's own) is 0 before the fixed first item, 1 while the home queue may hold items,
 // 2 after it ran out.  Other queues are probed by reading their counters first: counters only
-// grow, so one read at or past a queue's end proves that queue empty.
+// grow, so one read at or past a queue's end proves that queue empty.  With fixed_only (the fixed
+// first items cover every queue) no counter is read or written at all.
 __device__ __forceinline__ unsigned int claim_item(unsigned int* queue, int home, int& state, int splits,
-                                                   int row_blocks) {
+                                                   int row_blocks, bool fixed_only) {
   const unsigned int home_items = queue_items(splits, row_blocks, home);
   if (state == 0) {
     state = 1;
     const unsigned int c = blockIdx.x >> 3;
     if (c < home_items) return c * 8u + (unsigned int)home;
   }
+  if (fixed_only) return kNoItem;
   if (state == 1) {
-    const unsigned int c = atomicAdd(&queue[home], 1u) + queue_fixed(home);
+    const unsigned int c = atomicAdd(&queue[home], 1u) + queue_fixed(gridDim.x, home);
     if (c < home_items) return c * 8u + (unsigned int)home;
     state = 2;
   }
@@ -104,17 +120,23 @@ __device__ __forceinline__ unsigned int claim_item(unsigned int* queue, int home
     for (int d = 1; d < 8; ++d) {
       const int x = (home + d) & 7;
       const unsigned int taken = __hip_atomic_load(&queue[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (pick < 0 && taken + queue_fixed(x) < queue_items(splits, row_blocks, x)) pick = x;
+      if (pick < 0 && taken + queue_fixed(gridDim.x, x) < queue_items(splits, row_blocks, x)) pick = x;
     }
     if (pick < 0) return kNoItem;
-    const unsigned int c = atomicAdd(&queue[pick], 1u) + queue_fixed(pick);
+    const unsigned int c = atomicAdd(&queue[pick], 1u) + queue_fixed(gridDim.x, pick);
     if (c < queue_items(splits, row_blocks, pick)) return c * 8u + (unsigned int)pick;
   }
 }
 
+// Zeroes one launch's work-queue counters (a kernel rather than a memset node, so that the
+// pair captures into a graph as two kernel nodes).
+__global__ __launch_bounds__(64) void queue_clear_kernel(unsigned int* queue) {
+  if (threadIdx.x < kRaggedQueueWords) queue[threadIdx.x] = 0u;
+}
+
 template <int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogitsArgs a, int splits, int kps,
-                                                                       int slot) {
+                                                                       int use_queue) {
   constexpr int kThreads = 64 * WAVES;
   constexpr int kRows = 4 * WAVES;
   constexpr int kChunks = kTileKeys * (kDim / 16);   // 16-byte chunks per tile
@@ -133,7 +155,7 @@ __global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogi
   const int n = a.n;
   const bool clean = a.clean != 0;
   const int row_blocks = (a.m + kRows - 1) / kRows;
-  unsigned int* const queue = g_ragged_queue[slot];
+  unsigned int* const queue = a.queue;
 
   // Queue x holds the items of the splits x, x + 8, x + 16, ...: row blocks from the last (the
   // longest causal windows) to the first, each with all of the queue's splits.  Workgroups are
@@ -142,16 +164,14 @@ __global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogi
   // counters hand out the rest.  A workgroup whose queue is empty moves on
   // to a queue that is not.
   const int home = blockIdx.x & 7;
-  // When the fixed first items cover every queue, the counters are not needed at all.
-  bool fixed_only = true;
-#pragma unroll
-  for (int x = 0; x < 8; ++x)
-    fixed_only = fixed_only && queue_items(splits, row_blocks, x) <= queue_fixed(x);
+  // When the fixed first items cover every queue (the host checks this with the same formula),
+  // the counters are not needed at all.
+  const bool fixed_only = use_queue == 0;
   int claim_state = 0;
   for (;;) {
     __syncthreads();   // the previous item is done with s_ks/s_ke, the tiles and s_claim
     if (tid == 0) {
-      s_claim = fixed_only && claim_state > 0 ? kNoItem : claim_item(queue, home, claim_state, splits, row_blocks);
+      s_claim = claim_item(queue, home, claim_state, splits, row_blocks, fixed_only);
     }
     __syncthreads();
     const unsigned int claim = s_claim;
@@ -298,46 +318,18 @@ __global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogi
       }
     }
   }
-
-  // Every queue is empty for this workgroup.  The last one to get here resets the slot: by then no
-  // workgroup of this launch touches the counters again.  (With fixed items only, none touched them.)
-  if (tid == 0 && !fixed_only) {
-    __threadfence();
-    if (atomicAdd(&queue[8], 1u) == gridDim.x - 1) {
-#pragma unroll
-      for (int i = 0; i < 9; ++i) atomicExch(&queue[i], 0u);
-    }
-  }
 }
 
 void query_ragged_occupancy(DeviceInfo& d) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, logits_ragged_kernel<4>, 256, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, logits_ragged_kernel<kWaves>, 64 * kWaves, 0) != hipSuccess)
     per_cu = 1;
   d.ragged_wgs_per_cu = per_cu > 0 ? per_cu : 1;
 }
 
-// Work-queue slot of a stream: the first kQueueSlots streams get slots of their own; later ones
-// reuse the least recently assigned slot.
-static int queue_slot(hipStream_t s) {
-  static std::mutex mu;
-  static hipStream_t owner[kQueueSlots];
-  static int assigned = 0;
-  std::lock_guard<std::mutex> lock(mu);
-  const int used = std::min(assigned, kQueueSlots);
-  for (int i = 0; i < used; ++i)
-    if (owner[i] == s) return i;
-  const int slot = assigned % kQueueSlots;
-  owner[slot] = s;
-  ++assigned;
-  return slot;
-}
-
 hipError_t launch_logits_ragged(const RaggedLogitsArgs& a, const DeviceInfo& dev, hipStream_t s) {
   if (a.m <= 0) return hipSuccess;
-  constexpr int kWaves = 4;
-  constexpr int kRows = 4 * kWaves;
-  const int64_t row_blocks = (a.m + kRows - 1) / kRows;
+  const int64_t row_blocks = (a.m + kRowsPerItem - 1) / kRowsPerItem;
   // resident workgroups of this kernel on the whole device, rounded to XCDs
   const int per_cu = dev.ragged_wgs_per_cu > 0 ? dev.ragged_wgs_per_cu : 1;
   int64_t resident = (int64_t)(dev.cu_count > 0 ? dev.cu_count : 256) * per_cu;
@@ -353,9 +345,15 @@ hipError_t launch_logits_ragged(const RaggedLogitsArgs& a, const DeviceInfo& dev
   const int64_t items = row_blocks * splits;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
   const int64_t grid = std::min<int64_t>(items, resident);
-  const int slot = queue_slot(s);
+  const bool use_queue = queues_needed((unsigned int)grid, (int)splits, (int)row_blocks);
+  if (use_queue) {
+    if (a.queue == nullptr) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(queue_clear_kernel, dim3(1), dim3(64), 0, s, a.queue);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(logits_ragged_kernel<kWaves>, dim3((unsigned)grid), dim3(64 * kWaves), 0, s, a,
-                     (int)splits, (int)kps, slot);
+                     (int)splits, (int)kps, use_queue ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -119,7 +119,7 @@ __device__ __forceinline__ int32_t map_index(const TopkMap m, int req, int row_k
     const int64_t p = j / m.page_size;
     if (req < 0 || p >= m.ld) return -1;
     const int32_t page = m.table[(int64_t)req * m.ld + p];
-    if (page < 0) return -1;
+    if (page < 0 || page >= m.num_pages) return -1;
     return page * m.page_size + (j - (int32_t)p * m.page_size);
   }
   return j;
@@ -856,6 +856,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
 
 TopkPlan plan_topk(int32_t rows, int64_t width, int32_t k) {
   TopkPlan p{};
+  p.supported = true;
   p.buf_bytes[0] = p.buf_bytes[1] = 0;
   int64_t in_len = width > 0 ? width : 1;
   // few rows: split long windows so about this many workgroups run.  Every extra segment sends k
@@ -884,6 +885,8 @@ TopkPlan plan_topk(int32_t rows, int64_t width, int32_t k) {
     p.buf_bytes[lvl & 1] = std::max(p.buf_bytes[lvl & 1], bytes);
     in_len = out_len;
   }
+  // the last level writes the output row, so it must hold one segment per row
+  if (p.level[p.nlevels - 1].nseg > 1) p.supported = false;
   return p;
 }
 
@@ -915,6 +918,7 @@ static void launch_cap(bool level0, bool final_level, bool vec4, unsigned grid, 
 
 hipError_t launch_topk(const TopkArgs& ta, const TopkPlan& plan, void* ws, hipStream_t s) {
   if (ta.rows <= 0) return hipSuccess;
+  if (!plan.supported) return hipErrorInvalidValue;
   uint8_t* bufs[2] = {nullptr, nullptr};
   {
     uint8_t* w = static_cast<uint8_t*>(ws);

@@ -22,7 +22,9 @@
  * - Pointers: every array pointer is a DEVICE pointer (HIP device memory or
  *   memory the device can read) unless marked "host".  The caller owns all
  *   memory.  The library never allocates, frees or keeps device memory between
- *   calls; scratch comes only from the caller's `ws` buffer.
+ *   calls, and keeps no state that one call leaves for another: scratch
+ *   (work-queue counters, top-k candidates, chunk logits) comes only from the
+ *   caller's `ws` buffer, whose contents on entry do not matter.
  * - Layouts: row-major, contiguous in the last dimension; leading dimensions
  *   (in elements) are explicit where a buffer may be wider than its content.
  *   q, kv and kv pools must be 16-byte aligned; float and int32 arrays 4-byte
@@ -44,8 +46,10 @@
  * - kv_scale must be >= 0 (quantisation scales); NaN or infinite inputs give
  *   unspecified results.
  * - Determinism: identical inputs give identical output bytes.  Concurrent
- *   calls on different streams are safe when their outputs and workspaces do
- *   not overlap.
+ *   calls (on different streams, from different threads, or as replays of
+ *   captured graphs) are safe when their outputs and workspaces do not
+ *   overlap; a call's workspace must not be used by any other work while the
+ *   call's kernels run.
  * - Top-k output: each row holds the selected keys (a set: positions within
  *   the row are not part of the contract; this library writes them in
  *   ascending key order) followed by -1 padding when the row's window holds
@@ -96,13 +100,16 @@ typedef struct fp8idx_map {
                               (like cu_seqlens_q); NULL puts every row in request 0 */
   int32_t rows_per_req;    /* block table: consecutive rows per request (next_n) */
   int32_t page_size;       /* block table: keys per page */
+  int64_t num_pages;       /* block table: pages in the pool (>= 1); a page id outside
+                              [0, num_pages) maps its keys to -1 */
 } fp8idx_map;
 
 /* Operation selector for fp8idx_workspace_bytes(). */
 typedef enum fp8idx_op {
   FP8IDX_OP_TOPK = 0,              /* indexer_topk */
   FP8IDX_OP_LOGITS_TOPK_RAGGED = 1, /* indexer_logits_topk_ragged */
-  FP8IDX_OP_LOGITS_TOPK_RAGGED_OVERLAP = 2 /* indexer_logits_topk_ragged_overlap */
+  FP8IDX_OP_LOGITS_TOPK_RAGGED_OVERLAP = 2, /* indexer_logits_topk_ragged_overlap */
+  FP8IDX_OP_LOGITS_RAGGED = 3      /* indexer_logits_ragged (work-queue counters) */
 } fp8idx_op;
 
 /*
@@ -117,20 +124,19 @@ typedef enum fp8idx_op {
  *            the window); when clean == 0 only the window is guaranteed and
  *            other columns < n hold unspecified values.  Columns >= n are
  *            never touched.
- * m == 0 is a no-op.  Requires n >= 1, m >= 0.
- * Workgroups take their items from a device-side work queue that belongs to
- * the stream (a fixed table of 64 slots per device; each launch resets its
- * slot when it ends).  Launches on one stream, or replays of a captured
- * graph on one stream, never overlap and are always safe.  Launches that may
- * run at the same time must be on different streams; the first 64 streams
- * of the process get slots of their own, later ones share the least recently
- * assigned slot.  The same holds for the logits launches of the fused entries.
+ *   ws       device scratch of at least fp8idx_workspace_bytes(
+ *            FP8IDX_OP_LOGITS_RAGGED, m, n, 1, 0) bytes (256), 256-byte
+ *            aligned: the work-queue counters the kernel's workgroups claim
+ *            their items from.  The call clears them on `stream` before the
+ *            logits kernel, so their contents on entry do not matter; calls
+ *            that may run at the same time need distinct `ws` buffers.
+ * m == 0 is a no-op (ws may then be NULL).  Requires n >= 1, m >= 0.
  */
 FP8IDX_API fp8idx_status indexer_logits_ragged(const uint8_t* q, const uint8_t* kv, const float* kv_scale,
                                     const float* weights, const int32_t* ks, const int32_t* ke,
                                     int32_t m, int32_t n, int32_t H, int32_t D,
                                     float* logits, int64_t ld_logits, int32_t clean,
-                                    void* stream);
+                                    void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Paged-decode fp8 MQA logits (the paged form of the indexer named on the
@@ -146,6 +152,8 @@ FP8IDX_API fp8idx_status indexer_logits_ragged(const uint8_t* q, const uint8_t* 
  *   logits      [B * next_n, ld_logits] float32, width <= ld_logits columns
  *               are owned by the call: row r's window [0, min(row_len[r], width))
  *               is written, and with clean != 0 the rest of [0, width) is -inf.
+ *               Keys of the window whose page id lies outside [0, num_pages)
+ *               get -inf whatever `clean` says.
  * page_size must be 64.
  */
 FP8IDX_API fp8idx_status indexer_logits_paged(const uint8_t* q, const uint8_t* kv_pool,
@@ -171,7 +179,9 @@ FP8IDX_API fp8idx_status indexer_logits_paged(const uint8_t* q, const uint8_t* k
  *          rows, width, k, 0) bytes (rows longer than one selection segment,
  *          or few rows, are split into segments whose candidates live there;
  *          the size may be 0, and ws may then be NULL)
- * 1 <= k <= 16384.
+ * 1 <= k <= 16384.  Rows so long that the candidate merge would need more
+ * than 8 selection levels (width above about 2^30 at k = 16384) return
+ * FP8IDX_EUNSUPPORTED.
  */
 FP8IDX_API fp8idx_status indexer_topk(const float* logits, int64_t ld, int32_t rows, int32_t width,
                            const int32_t* ks, const int32_t* ke, int32_t k, int32_t row0,
@@ -187,6 +197,8 @@ FP8IDX_API fp8idx_status indexer_topk(const float* logits, int64_t ld, int32_t r
  *   logits_cap_bytes   0 = one chunk holding every row
  *   ws, ws_bytes       >= fp8idx_workspace_bytes(FP8IDX_OP_LOGITS_TOPK_RAGGED,
  *                        m, n, k, logits_cap_bytes)
+ * The workspace holds the logits kernel's work-queue counters (first 256
+ * bytes), one chunk of logits and the top-k candidates.
  * Other arguments as indexer_logits_ragged and indexer_topk (row0 = 0).
  */
 FP8IDX_API fp8idx_status indexer_logits_topk_ragged(const uint8_t* q, const uint8_t* kv,
@@ -211,10 +223,11 @@ FP8IDX_API fp8idx_status indexer_logits_topk_ragged(const uint8_t* q, const uint
  *   side_stream   a stream other than `stream` (else FP8IDX_EINVAL)
  *   ws_bytes      >= fp8idx_workspace_bytes(FP8IDX_OP_LOGITS_TOPK_RAGGED_OVERLAP,
  *                    m, n, k, logits_cap_bytes)
- * The entry keeps four events per device, created on its first call on that
- * device; calls of this entry that overlap on one device race on them.
- * Stream capture works as a fork (the side stream joins through the first
- * event) and a join (the final wait).
+ * The ordering uses four events that the call creates (without timing) and
+ * destroys before it returns; a wait enqueued on a stream keeps the state
+ * the event had when the wait was enqueued, so nothing outlives the call and
+ * concurrent calls share nothing.  Stream capture works as a fork (the side
+ * stream joins through the first event) and a join (the final wait).
  */
 FP8IDX_API fp8idx_status indexer_logits_topk_ragged_overlap(const uint8_t* q, const uint8_t* kv,
                                                  const float* kv_scale, const float* weights,
@@ -347,13 +360,67 @@ FP8IDX_API fp8idx_status indexer_sparse_mla(const uint16_t* q, const uint8_t* kv
                                             float sm_scale, float* out, float* lse, void* ws, size_t ws_bytes,
                                             void* stream);
 
+/* Entry points whose arguments fp8idx_validate_only() checks. */
+typedef enum fp8idx_entry {
+  FP8IDX_ENTRY_LOGITS_RAGGED = 0,             /* indexer_logits_ragged */
+  FP8IDX_ENTRY_LOGITS_PAGED = 1,              /* indexer_logits_paged */
+  FP8IDX_ENTRY_TOPK = 2,                      /* indexer_topk */
+  FP8IDX_ENTRY_LOGITS_TOPK_RAGGED = 3,        /* indexer_logits_topk_ragged */
+  FP8IDX_ENTRY_LOGITS_TOPK_RAGGED_OVERLAP = 4, /* indexer_logits_topk_ragged_overlap */
+  FP8IDX_ENTRY_LOGITS_TOPK_PAGED = 5          /* indexer_logits_topk_paged */
+} fp8idx_entry;
+
+/* The arguments of one call of an indexer entry point, field for field under
+ * the parameter names of the declarations above (indexer_topk's `logits`
+ * input is `scores` here, its `ld` is `ld_logits`).  Fields the entry does not
+ * take are ignored.  Host struct; pointers are only compared with NULL and
+ * tested for alignment, never dereferenced. */
+typedef struct fp8idx_call_args {
+  const uint8_t* q;
+  const uint8_t* kv;            /* kv, or kv_pool for the paged entries */
+  const float* kv_scale;        /* kv_scale, or scale_pool for the paged entries */
+  const float* weights;
+  const int32_t* ks;
+  const int32_t* ke;
+  const int32_t* row_len;
+  const int32_t* block_table;
+  int32_t m, n, H, D;
+  int32_t B, next_n, page_size, max_pages;
+  int64_t num_pages;
+  int32_t width;
+  float* logits;                /* output of the logits entries */
+  const float* scores;          /* input of indexer_topk */
+  int64_t ld_logits;
+  int32_t clean;
+  int32_t rows, k, row0, map_to_slots;
+  const fp8idx_map* map;
+  int32_t* out;
+  int64_t ld_out;
+  size_t logits_cap_bytes;
+  void* ws;
+  size_t ws_bytes;
+  void* stream;
+  void* side_stream;
+} fp8idx_call_args;
+
+/*
+ * Host-only argument check: the status `entry` would return for `args`
+ * before it looks for a device, i.e. every FP8IDX_EINVAL, FP8IDX_EUNSUPPORTED
+ * and FP8IDX_EWORKSPACE case, and FP8IDX_OK when the call would go on to the
+ * device.  The entry points run this same check first.  Touches no device
+ * and needs none (for tests and for callers that vet a configuration on a
+ * host without a GPU).  A NULL args or an unknown entry gives FP8IDX_EINVAL.
+ */
+FP8IDX_API fp8idx_status fp8idx_validate_only(int32_t entry, const fp8idx_call_args* args);
+
 /* Bytes of workspace indexer_sparse_mla needs (0 when it runs without
  * splitting the top-k lists).  Pure host arithmetic. */
 FP8IDX_API size_t fp8idx_sparse_mla_workspace_bytes(int32_t T, int32_t H, int32_t topk);
 
-/* Bytes of device workspace an operation needs (0 when it needs none).
- * rows = logits rows (m or B * next_n), width = keys per row (n or the
- * paged width).  Pure host arithmetic. */
+/* Bytes of device workspace an operation needs (0 when it needs none, or
+ * for arguments the operation rejects).  rows = logits rows (m or
+ * B * next_n), width = keys per row (n or the paged width); k is ignored for
+ * FP8IDX_OP_LOGITS_RAGGED.  Pure host arithmetic. */
 FP8IDX_API size_t fp8idx_workspace_bytes(int32_t op, int32_t rows, int64_t width, int32_t k,
                               size_t logits_cap_bytes);
 

@@ -34,7 +34,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.EXPORTED) == names
@@ -47,8 +47,8 @@ def test_status_strings(lib):
     assert lib.fp8idx_version().decode().startswith("fp8idx")
 
 
-def _ragged(lib, q=P, kv=P, sc=P, w=P, ks=P, ke=P, m=4, n=64, H=32, D=128, lg=P, ld=64, clean=1):
-    return lib.indexer_logits_ragged(q, kv, sc, w, ks, ke, m, n, H, D, lg, ld, clean, None)
+def _ragged(lib, q=P, kv=P, sc=P, w=P, ks=P, ke=P, m=4, n=64, H=32, D=128, lg=P, ld=64, clean=1, ws=P, wsb=256):
+    return lib.indexer_logits_ragged(q, kv, sc, w, ks, ke, m, n, H, D, lg, ld, clean, ws, wsb, None)
 
 
 def test_ragged_validation(lib):
@@ -63,7 +63,12 @@ def test_ragged_validation(lib):
     assert _ragged(lib, ld=63) == EINVAL          # ld < n
     assert _ragged(lib, m=-1) == EINVAL
     assert _ragged(lib, n=0) == EINVAL
-    assert _ragged(lib, m=0, q=NULL, lg=NULL) == OK   # empty call is a no-op
+    assert _ragged(lib, m=0, q=NULL, lg=NULL, ws=NULL, wsb=0) == OK   # empty call is a no-op
+    # the work-queue counters come from the workspace: 256 bytes, 256-byte aligned
+    assert lib.fp8idx_workspace_bytes(binding.OP_LOGITS_RAGGED, 4, 64, 1, 0) == 256
+    assert _ragged(lib, ws=NULL, wsb=0) == EWS
+    assert _ragged(lib, wsb=255) == EWS
+    assert _ragged(lib, ws=P + 128) == EINVAL
     # valid arguments but no gfx950 device in this process
     assert _ragged(lib) == EDEV
 
@@ -109,7 +114,12 @@ def test_topk_validation(lib):
     assert _topk(lib, mp=ctypes.byref(tok)) == EDEV
     blk = binding._CMap()
     blk.kind, blk.table, blk.ld, blk.num_req, blk.rows_per_req, blk.page_size = binding.MAP_BLOCK_TABLE, P, 4, 2, 0, 64
+    blk.num_pages = 100
     assert _topk(lib, mp=ctypes.byref(blk)) == EINVAL     # rows_per_req < 1
+    blk.rows_per_req = 4
+    assert _topk(lib, mp=ctypes.byref(blk)) == EDEV
+    blk.num_pages = 0
+    assert _topk(lib, mp=ctypes.byref(blk)) == EINVAL     # the pool's page count bounds page ids
     # a split plan needs workspace: few rows of a long window
     need = lib.fp8idx_workspace_bytes(binding.OP_TOPK, 2, 200000, 2048, 0)
     assert need > 0
@@ -154,8 +164,8 @@ def test_fused_workspace_covers_chunk_and_candidates(lib):
     cand = 2380 * 4 * 2048 * 8          # 4 segments of up to 52500 keys per row
     assert ws >= logits + cand
     assert ws <= logits + cand + 4096
-    # one-shot on 8192 x 65536: the full 2 GiB buffer, single-segment top-k
-    assert F.fp8idx_workspace_bytes(F.OP_LOGITS_TOPK_RAGGED, 8192, 65536, 2048, 0) == 8192 * 65536 * 4
+    # one-shot on 8192 x 65536: the work-queue counters and the full 2 GiB buffer, single-segment top-k
+    assert F.fp8idx_workspace_bytes(F.OP_LOGITS_TOPK_RAGGED, 8192, 65536, 2048, 0) == 256 + 8192 * 65536 * 4
 
 
 def test_quant_validation(lib):

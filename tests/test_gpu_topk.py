@@ -96,7 +96,7 @@ def test_block_table_map():
     ke = rng.integers(100, width + 1, rows).astype(np.int32)
     max_pages = (width + 63) // 64
     bt = rng.permutation(200)[: B * max_pages].astype(np.int32).reshape(B, max_pages)
-    m = F.TopkMap(kind=F.MAP_BLOCK_TABLE, table=to_dev(bt), rows_per_req=nn, page_size=64)
+    m = F.TopkMap(kind=F.MAP_BLOCK_TABLE, table=to_dev(bt), rows_per_req=nn, page_size=64, num_pages=200)
     g = _run_topk(x, None, ke, k, map_=m)
     raw = topk_indices(x, np.zeros(rows, np.int64), ke, k)
     e = map_block_table(raw, list(range(rows)), nn, bt, 64)
