@@ -26,6 +26,7 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     load_library,
     indexer_logits_ragged,
+    indexer_logits_ragged_noalloc,
     indexer_logits_paged,
     indexer_topk,
     indexer_logits_topk_ragged,

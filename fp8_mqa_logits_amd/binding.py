@@ -40,7 +40,7 @@ EXPORTED = (
     "indexer_quant_fp8", "indexer_logits_topk_ragged_overlap",
     "indexer_prepare_ragged", "indexer_prepare_decode",
     "indexer_sparse_mla", "fp8idx_sparse_mla_workspace_bytes", "fp8idx_probe_mfma_fp8",
-    "fp8idx_validate_only",
+    "fp8idx_validate_only", "indexer_logits_ragged_noalloc",
 )
 
 MLA_DQK = 576   # sparse MLA KV row: 512 latent + 64 rotary values
@@ -129,6 +129,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "fp8idx_sparse_mla_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
         "fp8idx_probe_mfma_fp8": (_I32, [_I32, _I32, _P, ctypes.POINTER(ctypes.c_double), _P]),
         "fp8idx_validate_only": (_I32, [_I32, ctypes.POINTER(CallArgs)]),
+        "indexer_logits_ragged_noalloc": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _I64, _I32,
+                                                 _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -390,6 +392,25 @@ def indexer_logits_ragged(q, kv, kv_scale, weights, ks, ke, *, clean: bool = Tru
             _ptr(q8), _ptr(kv8), _ptr(kv_scale), _ptr(weights), _ptr(ks), _ptr(ke), m, n, H, D,
             _ptr(logits), logits.shape[1], int(bool(clean)), wp, wb, _stream(dev, stream))
     _check("indexer_logits_ragged", st)
+    return logits
+
+
+def indexer_logits_ragged_noalloc(q, kv, kv_scale, weights, ks, ke, *, logits: torch.Tensor, clean: bool = True,
+                                  stream=None) -> torch.Tensor:
+    """indexer_logits_ragged into the caller's ``logits`` [m, ld >= n] with no allocation at all: the
+    work-queue counters are the library's static per-device array, so calls that may overlap in time
+    on one GPU race (use indexer_logits_ragged with distinct workspaces for those)."""
+    q8, kv8, m, n = _ragged_inputs(q, kv, kv_scale, weights, ks, ke)
+    _need(logits, "logits", _F32)
+    if logits.dim() != 2 or logits.shape[0] != m or logits.shape[1] < n:
+        raise ValueError(f"logits must be [{m}, >= {n}] float32, got {tuple(logits.shape)}")
+    dev = _dev(q8, "q")
+    _same_device(dev, kv=kv8, kv_scale=kv_scale, weights=weights, ks=ks, ke=ke, logits=logits)
+    with torch.cuda.device(dev):
+        st = load_library().indexer_logits_ragged_noalloc(
+            _ptr(q8), _ptr(kv8), _ptr(kv_scale), _ptr(weights), _ptr(ks), _ptr(ke), m, n, H, D,
+            _ptr(logits), logits.shape[1], int(bool(clean)), _stream(dev, stream))
+    _check("indexer_logits_ragged_noalloc", st)
     return logits
 
 

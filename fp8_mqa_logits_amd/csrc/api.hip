@@ -185,10 +185,17 @@ FusedLayout fused_layout(int32_t rows, int64_t width, int32_t k, size_t cap, int
 
 // ---- argument validation, shared by the entry points and fp8idx_validate_only ----------------
 
-fp8idx_status validate_logits_ragged(const fp8idx_call_args& c) {
+// Everything but the workspace (the allocation-free variant has none).
+fp8idx_status validate_logits_ragged_io(const fp8idx_call_args& c) {
   if (fp8idx_status s = check_ragged(c.q, c.kv, c.kv_scale, c.weights, c.ks, c.ke, c.m, c.n, c.H, c.D)) return s;
   if (c.m == 0) return FP8IDX_OK;
   if (!c.logits || !aligned(c.logits, 4) || c.ld_logits < c.n) return FP8IDX_EINVAL;
+  return FP8IDX_OK;
+}
+
+fp8idx_status validate_logits_ragged(const fp8idx_call_args& c) {
+  if (fp8idx_status s = validate_logits_ragged_io(c)) return s;
+  if (c.m == 0) return FP8IDX_OK;
   return check_ws(c.ws, c.ws_bytes, fp8idx::kRaggedQueueBytes);
 }
 
@@ -461,6 +468,25 @@ fp8idx_status indexer_logits_ragged(const uint8_t* q, const uint8_t* kv, const f
   if (fp8idx_status s = current_device(&dev)) return s;
   fp8idx::RaggedLogitsArgs a{q, kv, kv_scale, weights, ks, ke, m, n, logits, ld_logits, clean,
                              static_cast<unsigned int*>(ws)};
+  const hipError_t e = fp8idx::launch_logits_ragged(a, dev, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8IDX_OK : hip_fail(e);
+}
+
+fp8idx_status indexer_logits_ragged_noalloc(const uint8_t* q, const uint8_t* kv, const float* kv_scale,
+                                            const float* weights, const int32_t* ks, const int32_t* ke, int32_t m,
+                                            int32_t n, int32_t H, int32_t D, float* logits, int64_t ld_logits,
+                                            int32_t clean, void* stream) {
+  fp8idx_call_args c = ragged_call(q, kv, kv_scale, weights, ks, ke, m, n, H, D);
+  c.logits = logits;
+  c.ld_logits = ld_logits;
+  c.clean = clean;
+  if (fp8idx_status s = validate_logits_ragged_io(c)) return s;
+  if (m == 0) return FP8IDX_OK;
+  DeviceInfo dev;
+  if (fp8idx_status s = current_device(&dev)) return s;
+  unsigned int* queue = nullptr;
+  if (hipError_t e = fp8idx::ragged_noalloc_queue(&queue)) return hip_fail(e);
+  fp8idx::RaggedLogitsArgs a{q, kv, kv_scale, weights, ks, ke, m, n, logits, ld_logits, clean, queue};
   const hipError_t e = fp8idx::launch_logits_ragged(a, dev, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8IDX_OK : hip_fail(e);
 }

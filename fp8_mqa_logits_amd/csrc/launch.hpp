@@ -105,6 +105,9 @@ TopkPlan plan_topk(int32_t rows, int64_t width, int32_t k);
 size_t topk_workspace_bytes(const TopkPlan& p);
 
 hipError_t launch_logits_ragged(const RaggedLogitsArgs& a, const DeviceInfo& dev, hipStream_t s);
+// Device address of the current device's static work-queue counters (logits_ragged.hip), looked up
+// once per device; used by the entry point that allocates nothing.
+hipError_t ragged_noalloc_queue(unsigned int** out);
 hipError_t launch_logits_paged(const PagedLogitsArgs& a, const DeviceInfo& dev, hipStream_t s);
 constexpr int kPrepMaxReq = 4096;   // requests per index-preparation call
 struct PrepRaggedArgs {

@@ -50,6 +50,7 @@
 #include "mqa_core.hpp"
 
 #include <algorithm>
+#include <mutex>
 
 namespace fp8idx {
 
@@ -318,6 +319,33 @@ __global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogi
       }
     }
   }
+}
+
+// Work-queue counters of indexer_logits_ragged_noalloc, for callers that cannot allocate: one set
+// per device (each GPU holds its own copy of this array until the process ends), shared by every
+// call of that entry on the device.  Host code must not use the array's name as an address: it
+// names a host-side stand-in.  The device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned int scratch[kRaggedQueueBytes / sizeof(unsigned int)];
+
+constexpr int kScratchDevices = 64;
+static std::once_flag g_scratch_once[kScratchDevices];
+static unsigned int* g_scratch_ptr[kScratchDevices];
+static hipError_t g_scratch_err[kScratchDevices];
+
+hipError_t ragged_noalloc_queue(unsigned int** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? static_cast<unsigned int*>(ptr) : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 void query_ragged_occupancy(DeviceInfo& d) {

@@ -139,6 +139,25 @@ FP8IDX_API fp8idx_status indexer_logits_ragged(const uint8_t* q, const uint8_t* 
                                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * indexer_logits_ragged without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, layouts and
+ * results as indexer_logits_ragged, minus ws / ws_bytes.
+ * The work-queue counters live in a static device array of the library
+ * (256 bytes per device, held until the process ends), cleared on `stream`
+ * by each call that needs them; nothing is allocated and no size is too
+ * large for it, since the counters do not grow with m or n.  Every call of
+ * this entry on one GPU shares that array: calls that may overlap in time
+ * on one GPU (different streams, threads, or concurrent graph replays)
+ * race and must use indexer_logits_ragged with distinct workspaces.
+ */
+FP8IDX_API fp8idx_status indexer_logits_ragged_noalloc(const uint8_t* q, const uint8_t* kv, const float* kv_scale,
+                                                       const float* weights, const int32_t* ks, const int32_t* ke,
+                                                       int32_t m, int32_t n, int32_t H, int32_t D,
+                                                       float* logits, int64_t ld_logits, int32_t clean,
+                                                       void* stream);
+
+/*
  * Paged-decode fp8 MQA logits (the paged form of the indexer named on the
  * vessl-ai/sglang PR #87 page).  B requests of next_n query rows each; row
  * r = b * next_n + t belongs to request b and sees keys [0, row_len[r]).

@@ -34,7 +34,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.EXPORTED) == names
@@ -69,6 +69,16 @@ def test_ragged_validation(lib):
     assert _ragged(lib, ws=NULL, wsb=0) == EWS
     assert _ragged(lib, wsb=255) == EWS
     assert _ragged(lib, ws=P + 128) == EINVAL
+    # the allocation-free variant: the same checks without a workspace
+    nf = lambda **kw: lib.indexer_logits_ragged_noalloc(*[kw.get(k, P) for k in ("q", "kv", "sc", "w", "ks", "ke")],
+                                                        kw.get("m", 4), 64, kw.get("H", 32), 128,
+                                                        kw.get("lg", P), kw.get("ld", 64), 1, None)
+    assert nf(H=16) == EUNSUP
+    assert nf(q=NULL) == EINVAL
+    assert nf(lg=NULL) == EINVAL
+    assert nf(ld=63) == EINVAL
+    assert nf(m=0, q=NULL, lg=NULL) == OK
+    assert nf() == EDEV
     # valid arguments but no gfx950 device in this process
     assert _ragged(lib) == EDEV
 
