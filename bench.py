@@ -3,19 +3,36 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step = the whole hot path over one synthetic batch: the ragged fp8 MQA
-logits of every query row followed by the per-row top-k, i.e. exactly the two
-kernel launches the fused entry makes when its logits cap holds all rows
-(the chunking page's one-shot reference; its production cap of 8 GB also
-gives one chunk here).  Inputs are resident in HBM before timing starts.
-Rank 0 prints one JSON line.
+One step = the whole hot path over one synthetic batch: the fused C entry
+(indexer_logits_topk_ragged, or indexer_logits_topk_paged for the decode
+workload), which per row chunk launches the fp8 MQA logits into its workspace
+and then the per-row top-k.  The default workload is the largest one, the
+long prefix of the chunking page's `warm_long_150K+60K` scenario: 7500 query
+rows over 210000 keys under the 2e9-byte logits cap (4 chunks of 2380, 2380,
+2380 and 360 rows).  Inputs are resident in HBM before timing starts.  Rank 0
+prints one JSON line.
+
+Two timed regions run back to back, each after its own warm-up and each
+bracketed by synchronisations:
+  1. K steps of the fused entry: `value`, `ms_per_step` and the per-step
+     event distribution;
+  2. K steps of the same launches made one call at a time (the logits entry
+     into the same chunk buffer, then the top-k entry), with HIP events on the
+     launch stream between them: the per-launch durations behind `roofline`
+     (`split_ms_per_step` shows that both regions do the same work).
+Under `rocprofv3 --selected-regions` only these two regions are traced
+(roctxProfilerResume / Pause around them).
 
 Extra modes (used to collect counters and cross-checks):
-  --fused-check        also time the fused C entry and report its ms/step
   --no-cpu-baseline    skip the oracle timing (profiling runs)
   --copy-calibration   only run a plain device copy of known size (for
                        scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
-  --all-workloads PATH time every workload and write a JSON list to PATH
+  --all-workloads PATH time every workload, with the oracle beside each,
+                       and write a JSON list to PATH
+  --trace-summary CSV  (no GPU) summarise a rocprofv3 kernel_trace.csv or
+                       counter_collection.csv of a run of this script made
+                       with the same --steps / --warmup: per kernel, only the
+                       dispatches of the timed steps of both regions
 """
 
 from __future__ import annotations
@@ -53,14 +70,14 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill_64k")
+    ap.add_argument("--workload", default="long_prefix_210k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the on-box MFMA and copy peak probes")
     ap.add_argument("--cold", action="store_true",
                     help="rewrite a 512 MiB scratch buffer before each timed step (cold caches)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--fused-check", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--trace-summary", default="", metavar="CSV")
     ap.add_argument("--all-workloads", default="")
     ap.add_argument("--overlap", action="store_true", help="time the fused loop serial vs overlapped")
     ap.add_argument("--prep", action="store_true", help="time index preparation at the PR page's shapes")
@@ -98,9 +115,13 @@ class RaggedStep:
         self.ws_logits = torch.empty(512, dtype=torch.uint8, device="cuda")
         self.out = torch.empty((m, k), dtype=torch.int32, device="cuda")
         fws = F.fp8idx_workspace_bytes(F.OP_LOGITS_TOPK_RAGGED, m, n, k, self.cap)
-        self.fused_ws = None
-        self.fused_ws_bytes = fws
+        self.fused_ws = torch.empty(fws + 256, dtype=torch.uint8, device="cuda")
         self.events = []
+        import numpy as np
+        pairs = np.maximum(inp.ke.astype(np.int64) - inp.ks, 0)
+        # algorithmic flops of each chunk's logits launch: 2 * H * D per valid (row, key) pair
+        self.chunk_flops = [2.0 * H * D * float(pairs[s:s + self.rpc].sum()) for s in range(0, m, self.rpc)]
+        self.entry = "indexer_logits_topk_ragged"
 
     def run(self, record=False):
         """One pass of the hot path: per chunk, logits launch then top-k launch."""
@@ -123,9 +144,6 @@ class RaggedStep:
                 self.events.append((ev, e - s))
 
     def run_fused(self):
-        import torch
-        if self.fused_ws is None:
-            self.fused_ws = torch.empty(self.fused_ws_bytes + 256, dtype=torch.uint8, device="cuda")
         self.F.indexer_logits_topk_ragged(self.q, self.kv, self.sc, self.w, self.ks, self.ke, self.inp.k,
                                           logits_cap_bytes=self.cap, out=self.out, workspace=self.fused_ws)
 
@@ -142,10 +160,14 @@ class RaggedStep:
                                                   out=self.out, workspace=self.overlap_ws)
 
     def kernel_times(self):
-        """Average logits and top-k launch durations (ms) over the recorded launches."""
+        """Mean logits and top-k launch durations (ms) over the recorded launches, and their count."""
         lt = [ev[0].elapsed_time(ev[1]) for ev, _ in self.events]
         tt = [ev[1].elapsed_time(ev[2]) for ev, _ in self.events]
         return sum(lt) / len(lt), sum(tt) / len(tt), len(lt)
+
+    def logits_flops_per_launch(self):
+        """Mean algorithmic flops of one logits launch (the chunks' mean)."""
+        return sum(self.chunk_flops) / len(self.chunk_flops)
 
     def flops(self):
         return 2.0 * H * D * self.inp.valid_pairs
@@ -172,9 +194,10 @@ class PagedStep:
         m = F.TopkMap(kind=F.MAP_BLOCK_TABLE, table=self.args[5], rows_per_req=inp.next_n, page_size=64,
                       num_pages=inp.kv_pool.shape[0])
         self.map = m
-        self.fused_ws_bytes = F.fp8idx_workspace_bytes_paged(inp.B, inp.next_n, self.width, inp.k, 0)
-        self.fused_ws = None
+        fws = F.fp8idx_workspace_bytes_paged(inp.B, inp.next_n, self.width, inp.k, 0)
+        self.fused_ws = torch.empty(fws + 256, dtype=torch.uint8, device="cuda")
         self.events = []
+        self.entry = "indexer_logits_topk_paged"
 
     def run(self, record=False):
         import torch
@@ -192,9 +215,6 @@ class PagedStep:
             self.events.append((ev, inp.rows))
 
     def run_fused(self):
-        import torch
-        if self.fused_ws is None:
-            self.fused_ws = torch.empty(self.fused_ws_bytes + 256, dtype=torch.uint8, device="cuda")
         self.F.indexer_logits_topk_paged(*self.args, self.inp.k, width=self.width, out=self.out,
                                          workspace=self.fused_ws)
 
@@ -214,9 +234,48 @@ class PagedStep:
         return 4.0 * self.inp.valid_pairs + 4.0 * self.inp.rows * self.inp.k
 
 
+class Roctx:
+    """roctxProfilerResume / roctxProfilerPause (rocprofiler-sdk), so that a run under
+    `rocprofv3 --selected-regions` traces the timed regions only.  Without the profiler the calls do
+    nothing; without the library they are skipped."""
+
+    def __init__(self):
+        import ctypes
+        self.lib = None
+        for name in ("librocprofiler-sdk-roctx.so.1", "librocprofiler-sdk-roctx.so"):
+            try:
+                self.lib = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        if self.lib is not None:
+            for fn in ("roctxProfilerPause", "roctxProfilerResume"):
+                getattr(self.lib, fn).argtypes = [ctypes.c_uint64]
+                getattr(self.lib, fn).restype = ctypes.c_int
+
+    def pause(self):
+        if self.lib is not None:
+            self.lib.roctxProfilerPause(0)
+
+    def resume(self):
+        if self.lib is not None:
+            self.lib.roctxProfilerResume(0)
+
+
+ROCTX = None
+
+
+def _roctx():
+    global ROCTX
+    if ROCTX is None:
+        ROCTX = Roctx()
+    return ROCTX
+
+
 def _time_steps(step, steps, warmup, record, cold=False):
-    """Wall ms per step over `steps` timed steps; with record, per-launch and per-step HIP events
-    (on the launch stream) are kept on the step for the kernel times and the step distribution.
+    """Wall ms per step over `steps` timed steps of the launches made one call at a time; with
+    record, per-launch and per-step HIP events (on the launch stream) are kept on the step for the
+    kernel times and the step distribution.
 
     cold: before every step a 512 MiB scratch buffer is rewritten (more than the 256 MB Infinity
     Cache), so each step starts with cold caches; the flush lies outside the step events, and the
@@ -228,6 +287,7 @@ def _time_steps(step, steps, warmup, record, cold=False):
     torch.cuda.synchronize()
     step.events = []
     step.step_events = []
+    _roctx().resume()
     t0 = time.perf_counter()
     for i in range(steps):
         if cold:
@@ -240,9 +300,11 @@ def _time_steps(step, steps, warmup, record, cold=False):
             se[1].record()
             step.step_events.append(se)
     torch.cuda.synchronize()
+    t = time.perf_counter() - t0
+    _roctx().pause()
     if cold and record:
         return sum(e[0].elapsed_time(e[1]) for e in step.step_events) / steps
-    return (time.perf_counter() - t0) * 1e3 / steps
+    return t * 1e3 / steps
 
 
 def _median(xs):
@@ -251,9 +313,9 @@ def _median(xs):
     return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
 
 
-def _distribution(step):
-    """Median and min of the step and per-launch kernel times (ms) of the last timed run."""
-    st = [e[0].elapsed_time(e[1]) for e in step.step_events]
+def _distribution(step, fused_events):
+    """Median and min of the fused step times and of the per-launch kernel times (ms)."""
+    st = [e[0].elapsed_time(e[1]) for e in fused_events]
     lt = [ev[0].elapsed_time(ev[1]) for ev, _ in step.events]
     tt = [ev[1].elapsed_time(ev[2]) for ev, _ in step.events]
     return {"step_ms_median": round(_median(st), 4), "step_ms_min": round(min(st), 4),
@@ -305,21 +367,37 @@ def measured_peaks():
             "copy_probe": f"1 GiB device copy, read + written bytes, {reps} copies"}
 
 
-def _time_fused(step, steps, warmup, overlap=False):
+def _time_fused(step, steps, warmup, overlap=False, cold=False):
+    """(wall ms per step, per-step event pairs) over `steps` calls of the fused entry (or the
+    overlapped one), each step bracketed by HIP events on the calling stream."""
     import torch
     run = step.run_overlap if overlap else step.run_fused
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if cold else None
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
+    evs = []
+    _roctx().resume()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
+        if cold:
+            scratch.fill_(i & 0xff)
+        e = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+        e[0].record()
         run()
+        e[1].record()
+        evs.append(e)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+    t = time.perf_counter() - t0
+    _roctx().pause()
+    if cold:
+        return sum(a.elapsed_time(b) for a, b in evs) / steps, evs
+    return t * 1e3 / steps, evs
 
 
-def _traffic(kernel_key):
-    """HBM bytes per launch from the committed counter runs, if they match these kernel sources."""
+def _traffic(workload, kernel_key):
+    """HBM bytes per launch of a kernel on a workload from the committed counter runs, if they were
+    taken on these kernel sources."""
     try:
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
@@ -327,33 +405,18 @@ def _traffic(kernel_key):
         return None
     if c.get("kernel_source_hash") != kernel_source_hash():
         return None
-    k = c.get("kernels", {}).get(kernel_key)
+    k = c.get("workloads", {}).get(workload, {}).get(kernel_key)
     if not k:
         return None
     return k.get("hbm_bytes_per_launch")
 
 
-def _cpu_baseline(inp, budget_s):
-    """Time the float64 oracle (logits + top-k) on an evenly spaced row sample."""
-    import numpy as np
-    from oracle import mqa_logits, topk_indices
+def _cpu_info():
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    order = np.linspace(0, inp.m - 1, num=min(inp.m, 4096)).astype(np.int64)
-    done, valid, t_total = 0, 0, 0.0
-    block = 8
-    while done < order.size and (t_total < budget_s or done < 8):
-        rows = order[done:done + block]
-        t0 = time.perf_counter()
-        L = mqa_logits(inp.q[rows], inp.kv, inp.kv_scale, inp.weights[rows], inp.ks[rows], inp.ke[rows])
-        topk_indices(L, inp.ks[rows], inp.ke[rows], inp.k)
-        t_total += time.perf_counter() - t0
-        valid += int((inp.ke[rows].astype(np.int64) - inp.ks[rows]).clip(min=0).sum())
-        done += rows.size
-    tflops = 2.0 * H * D * valid / t_total / 1e12
     cpu_model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -363,40 +426,65 @@ def _cpu_baseline(inp, budget_s):
                     break
     except OSError:  # pragma: no cover
         pass
-    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "cpu_model": cpu_model,
-            "sample": f"{done} evenly spaced rows of {inp.m} ({valid} valid (row, key) pairs), "
-                      f"float64 logits + top-k, {t_total:.1f} s; ms/layer-equivalent "
-                      f"{t_total * 1e3 * inp.valid_pairs / max(valid, 1):.0f}"}
+    return int(threads), cpu_model
 
 
-def run_workload(name, steps, warmup, fused_check, cold=False):
+def _cpu_baseline(inp, budget_s):
+    """Time the float64 oracle (logits + top-k) on an evenly spaced row sample of the workload,
+    scaled to the whole workload (TFLOP/s and the ms/layer it implies)."""
+    import numpy as np
+    from oracle import mqa_logits, paged_mqa_logits, topk_indices
+    paged = hasattr(inp, "kv_pool")
+    rows_total = inp.rows if paged else inp.m
+    lens = inp.row_len.astype(np.int64) if paged else np.maximum(inp.ke.astype(np.int64) - inp.ks, 0)
+    order = np.linspace(0, rows_total - 1, num=min(rows_total, 4096)).astype(np.int64)
+    order = np.unique(order)
+    width = inp.max_pages * inp.page_size if paged else None
+    done, valid, t_total = 0, 0, 0.0
+    block = 8
+    while done < order.size and (t_total < budget_s or done < 8):
+        rows = order[done:done + block]
+        t0 = time.perf_counter()
+        if paged:
+            L = paged_mqa_logits(inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len, inp.block_table,
+                                 inp.page_size, width=width, rows=rows)
+            topk_indices(L, np.zeros(rows.size, np.int64), inp.row_len[rows], inp.k)
+        else:
+            L = mqa_logits(inp.q[rows], inp.kv, inp.kv_scale, inp.weights[rows], inp.ks[rows], inp.ke[rows])
+            topk_indices(L, inp.ks[rows], inp.ke[rows], inp.k)
+        t_total += time.perf_counter() - t0
+        valid += int(lens[rows].sum())
+        done += rows.size
+    tflops = 2.0 * H * D * valid / t_total / 1e12
+    threads, cpu_model = _cpu_info()
+    ms_layer = t_total * 1e3 * inp.valid_pairs / max(valid, 1)
+    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model, "ms_per_layer_equivalent": round(ms_layer, 1),
+            "sample": f"{done} evenly spaced rows of {rows_total} ({valid} valid (row, key) pairs), "
+                      f"float64 logits + top-k, {t_total:.1f} s, scaled to all "
+                      f"{inp.valid_pairs} pairs"}
+
+
+def run_workload(name, steps, warmup, cold=False, overlap=False):
+    """Both timed regions on one workload: the fused entry (step time), then the same launches one
+    call at a time with per-launch events (kernel times)."""
     import torch
     from workloads.generate import config_inputs
     inp = config_inputs(name)
     paged = hasattr(inp, "kv_pool")
     step = PagedStep(inp) if paged else RaggedStep(inp)
     torch.cuda.synchronize()
-    ms = _time_steps(step, steps, warmup, record=True, cold=cold)
+    fused_ms, fused_events = _time_fused(step, steps, warmup, cold=cold)
+    split_ms = _time_steps(step, steps, warmup, record=True, cold=cold)
     logit_ms, topk_ms, launches = step.kernel_times()
     per_step = launches // steps
-    # per-launch averages times launches per step = kernel time per step (chunked workloads
-    # make one logits and one top-k launch per chunk)
-    res = {"workload": inp.name, "ms_per_step": ms, "logits_ms": logit_ms * per_step,
-           "topk_ms": topk_ms * per_step, "logits_ms_per_launch": logit_ms, "topk_ms_per_launch": topk_ms,
-           "launches_per_step": per_step, "flops": step.flops(), "inp": inp, "step": step}
-    if fused_check:
-        res["fused_ms_per_step"] = _time_fused(step, steps, warmup)
-        if hasattr(step, "run_overlap") and step.rpc < inp.m:
-            res["overlap_ms_per_step"] = _time_fused(step, steps, warmup, overlap=True)
+    res = {"workload": inp.name, "entry": step.entry, "ms_per_step": fused_ms, "split_ms_per_step": split_ms,
+           "logits_ms": logit_ms * per_step, "topk_ms": topk_ms * per_step, "logits_ms_per_launch": logit_ms,
+           "topk_ms_per_launch": topk_ms, "launches_per_step": per_step, "flops": step.flops(),
+           "fused_events": fused_events, "inp": inp, "step": step}
+    if overlap and not paged and step.rpc < inp.m:
+        res["overlap_ms_per_step"], _ = _time_fused(step, steps, warmup, overlap=True)
     return res
-
-
-QUANT_SHAPES = (
-    ("kv_n65536_d128", 65536, 128),          # the 65536-key prefill's kv (per-token scales)
-    ("q_m8192_h32_d128", 8192 * 32, 128),    # its q, one row per (query row, head)
-    ("kv_n210000_d128", 210000, 128),        # the long-prefix workload's kv
-)
 
 
 def quant_workloads(steps, warmup):
@@ -581,11 +669,76 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 3}), flush=True)
 
 
+def _timed_dispatches(n, steps, warmup):
+    """Positions of the timed dispatches among a kernel's n dispatches in one run of this script.
+
+    Each of the two timed regions runs `warmup` steps, then `steps` timed steps, of identical
+    launches, so a kernel launched c times per step has n = 2 * (warmup + steps) * c dispatches, in
+    the order [warm-up, timed] of the fused region, then [warm-up, timed] of the call-by-call one.
+    Returns None when n does not fit that pattern (a kernel outside the timed regions)."""
+    per = 2 * (warmup + steps)
+    if n == 0 or n % per:
+        return None
+    c = n // per
+    first = list(range(warmup * c, (warmup + steps) * c))
+    second = list(range((2 * warmup + steps) * c, (2 * warmup + 2 * steps) * c))
+    return first + second
+
+
+def trace_summary(path, steps, warmup):
+    """Markdown summary of a rocprofv3 per-dispatch CSV restricted to the timed dispatches."""
+    import csv
+    from collections import OrderedDict
+    with open(path, newline="") as f:
+        rows = list(csv.DictReader(f))
+    out = []
+    if rows and "Counter_Name" in rows[0]:
+        # counter_collection.csv: one row per (dispatch, counter)
+        by = OrderedDict()
+        for r in rows:
+            by.setdefault(r["Kernel_Name"], OrderedDict()).setdefault(int(r["Dispatch_Id"]), {})[
+                r["Counter_Name"]] = float(r["Counter_Value"])
+        out.append("| kernel | dispatches (timed / all) | counter | mean per timed dispatch |")
+        out.append("|---|---|---|---|")
+        for name, disp in by.items():
+            ids = sorted(disp)
+            sel = _timed_dispatches(len(ids), steps, warmup)
+            if sel is None:
+                continue
+            counters = sorted({c for d in disp.values() for c in d})
+            for cn in counters:
+                vals = [disp[ids[i]].get(cn, 0.0) for i in sel]
+                out.append(f"| `{name}` | {len(sel)} / {len(ids)} | {cn} | {sum(vals) / len(vals):.6g} |")
+        return "\n".join(out)
+    by = OrderedDict()
+    for r in rows:
+        by.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out.append("| kernel | timed dispatches | mean us | median us | min us | max us | all dispatches | mean us (all) |")
+    out.append("|---|---|---|---|---|---|---|---|")
+    for name, ds in by.items():
+        ds.sort()
+        durs = [d for _, d in ds]
+        sel = _timed_dispatches(len(durs), steps, warmup)
+        allm = sum(durs) / len(durs) / 1e3
+        if sel is None:
+            out.append(f"| `{name}` | outside the timed regions | | | | | {len(durs)} | {allm:.2f} |")
+            continue
+        t = sorted(durs[i] for i in sel)
+        out.append(f"| `{name}` | {len(t)} | {sum(t) / len(t) / 1e3:.2f} | {_median(t) / 1e3:.2f} | "
+                   f"{t[0] / 1e3:.2f} | {t[-1] / 1e3:.2f} | {len(durs)} | {allm:.2f} |")
+    return "\n".join(out)
+
+
 def main():
     a = _args()
+    if a.trace_summary:
+        print(trace_summary(a.trace_summary, a.steps, a.warmup))
+        return
+    _roctx()   # load the marker library before the GPU runtime starts
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}); "
-              "the indexer path is rank-local, see the sharding notes in DESIGN.md", file=sys.stderr)
+              "the indexer path is rank-local: every rank runs this same single-GPU path on its own rows", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
@@ -599,14 +752,18 @@ def main():
     if a.all_workloads:
         rows = []
         for name in ("tiny", "prefill_64k", "prefill_35k", "paged_decode", "long_prefix_210k"):
-            r = run_workload(name, a.steps, a.warmup, True)
+            r = run_workload(name, a.steps, a.warmup, overlap=True)
             inp, step = r.pop("inp"), r.pop("step")
+            r.pop("fused_events")
             r["logits_tflops"] = r["flops"] / (r["logits_ms"] * 1e-3) / 1e12
             r["logits_mfma_frac"] = r["logits_tflops"] * 1e12 / MFMA_FP8_PEAK
             r["topk_gbps"] = step.topk_bytes() / (r["topk_ms"] * 1e-3) / 1e9
+            r["topk_hbm_frac"] = r["topk_gbps"] * 1e9 / HBM_PEAK
             if hasattr(step, "kv_bytes"):
                 r["logits_hbm_gbps"] = step.kv_bytes() / (r["logits_ms"] * 1e-3) / 1e9
                 r["logits_hbm_frac"] = r["logits_hbm_gbps"] * 1e9 / HBM_PEAK
+            if not a.no_cpu_baseline:
+                r["cpu_baseline"] = _cpu_baseline(inp, a.cpu_seconds)
             rows.append(r)
             print(json.dumps(r), file=sys.stderr, flush=True)
             del inp, step
@@ -626,8 +783,8 @@ def main():
                 inp.cap_bytes = cap
                 inp.name = f"{inp.name}_cap2GB"
             step = RaggedStep(inp)
-            serial = _time_fused(step, a.steps, a.warmup)
-            over = _time_fused(step, a.steps, a.warmup, overlap=True)
+            serial, _ = _time_fused(step, a.steps, a.warmup)
+            over, _ = _time_fused(step, a.steps, a.warmup, overlap=True)
             print(json.dumps({"workload": inp.name, "chunks": -(-inp.m // step.rpc), "rows_per_chunk": step.rpc,
                               "fused_serial_ms": round(serial, 4), "fused_overlap_ms": round(over, 4),
                               "overlap_gain": round(serial / over - 1, 4)}), flush=True)
@@ -647,20 +804,24 @@ def main():
             print(json.dumps(q), flush=True)
         return
 
-    r = run_workload(a.workload, a.steps, a.warmup, a.fused_check, cold=a.cold)
+    r = run_workload(a.workload, a.steps, a.warmup, cold=a.cold)
     inp, step = r["inp"], r["step"]
     flops = r["flops"]
-    logit_tflops = flops / (r["logits_ms"] * 1e-3) / 1e12
     paged = hasattr(inp, "kv_pool")
     if paged:
-        achieved = step.kv_bytes() / (r["logits_ms"] * 1e-3) / 1e9
+        # HBM bound: kv + scales of every referenced key, q, weights, block-table entries and the
+        # logits written, over the logits launch
+        achieved = step.kv_bytes() / (r["logits_ms_per_launch"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": _traffic("logits_paged")}
-        metric_value, unit = achieved, "GB/s"
+                "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": _traffic(inp.name, "logits_paged")}
+        metric_value, unit = step.kv_bytes() / (r["ms_per_step"] * 1e-3) / 1e9, "GB/s"
     else:
-        roof = {"bound": "mfma", "achieved": round(logit_tflops, 2), "peak": MFMA_FP8_PEAK / 1e12,
-                "unit": "TFLOP/s", "frac": round(logit_tflops * 1e12 / MFMA_FP8_PEAK, 4),
-                "traffic": _traffic("logits_ragged")}
+        # MFMA bound: 2 * H * D flops per valid (row, key) pair; the mean logits launch of a step
+        # (chunks of unequal size) against the mean launch duration
+        achieved = step.logits_flops_per_launch() / (r["logits_ms_per_launch"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_FP8_PEAK / 1e12,
+                "unit": "TFLOP/s", "frac": round(achieved * 1e12 / MFMA_FP8_PEAK, 4),
+                "traffic": _traffic(inp.name, "logits_ragged")}
         metric_value, unit = flops / (r["ms_per_step"] * 1e-3) / 1e12, "TFLOP/s"
     out = {
         "metric": "indexer logits+top-k ms/layer & TFLOP/s (prefill), GB/s (decode), % roofline",
@@ -675,23 +836,26 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8",
         "data": "synthetic",
-        "config": {"workload": inp.name, "caches": "cold" if a.cold else "warm"},
+        "config": {"workload": inp.name, "entry": r["entry"], "caches": "cold" if a.cold else "warm"},
         "roofline": roof,
         "logits_ms": round(r["logits_ms"], 4),
         "topk_ms": round(r["topk_ms"], 4),
+        "split_ms_per_step": round(r["split_ms_per_step"], 4),
+        "launches_per_step": r["launches_per_step"],
+        "logits_ms_per_launch": round(r["logits_ms_per_launch"], 4),
         "topk_gbps": round(step.topk_bytes() / (r["topk_ms"] * 1e-3) / 1e9, 1),
         "kernel_source_hash": kernel_source_hash(),
     }
     if paged:
         out["config"].update({"requests": inp.B, "rows_per_request": inp.next_n, "page_size": inp.page_size,
                               "k": inp.k, "width": step.width, "valid_pairs": inp.valid_pairs})
+        out["logits_hbm_bytes_per_launch"] = step.kv_bytes()
     else:
         out["config"].update({"m": inp.m, "n": inp.n, "H": H, "D": D, "k": inp.k,
                               "logits_cap_bytes": inp.cap_bytes, "rows_per_chunk": step.rpc,
-                              "valid_pairs": inp.valid_pairs})
-    out.update(_distribution(step))
-    if "fused_ms_per_step" in r:
-        out["fused_ms_per_step"] = round(r["fused_ms_per_step"], 4)
+                              "chunks": len(step.chunk_flops), "valid_pairs": inp.valid_pairs})
+        out["logits_flops_per_launch"] = step.logits_flops_per_launch()
+    out.update(_distribution(step, r["fused_events"]))
     if not a.no_peaks:
         pk = measured_peaks()
         if paged:
@@ -699,7 +863,7 @@ def main():
         else:
             pk["logits_frac_of_mfma_probe"] = round(roof["achieved"] / pk["mfma_fp8_tflops"], 4)
         out["measured_peaks"] = pk
-    if not a.no_cpu_baseline and not paged:
+    if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(inp, a.cpu_seconds)
     print(json.dumps(out), flush=True)
 
