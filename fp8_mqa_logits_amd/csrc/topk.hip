@@ -37,7 +37,11 @@
 // If the sample misjudges (fewer than k candidates, or more than fit), the
 // same exact selection and ordering run over every key of the segment,
 // streamed from memory once per step.
-// Rows longer than one segment, or few rows that need more parallelism, are
+// Few long rows (at most 512 rows of at most 131072 keys, k up to about
+// 2800: paged decode) take one 512-thread workgroup per whole row instead:
+// twice the loads in flight of a 256-thread segment, a single launch and no
+// merge level (position bitmaps sized for 131072 keys, two workgroups per CU).
+// Other rows longer than one segment, or few rows that need more parallelism, are
 // split: each segment emits its local top-k (code, index) pairs in index
 // order, and further levels of the same kernel select from the concatenated
 // pairs (still in index order, so position order is index order).  Because
@@ -79,13 +83,17 @@ struct TopkKernelArgs {
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
 constexpr int64_t kMaxSeg = 65536;                                // keys per segment
-constexpr int kBitmapWords = (int)((kMaxSeg + 4 + 31) / 32) + 1;  // positions from the 16-byte load base
+// Position bitmap words of a segment of up to `seg` keys (positions count from the 16-byte load base).
+constexpr int bitmap_words(int64_t seg) { return (int)((seg + 4 + 31) / 32) + 1; }
+constexpr int kBitmapWords = bitmap_words(kMaxSeg);
 constexpr int kTopkThreads = 256;
 constexpr int kSampleRuns = 16;
-constexpr int kSampleSize = kSampleRuns * kTopkThreads;
+// Few long rows: one wide workgroup per whole row (no merge level).
+constexpr int kWideThreads = 512;
+constexpr int64_t kWideSeg = 131072;
+constexpr int kWideRowsMax = 512;
 constexpr int kElemsPerPass = 32;   // keys a thread loads per streaming pass
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-constexpr int kBoundaryMax = kTopkThreads;   // boundary-bin candidates ranked pairwise
 
 // Candidate-list capacity for k: the expected list (1.3 k + 24 sample units
 // of keys, at most 384 keys) must stay under 7/8 of it.
@@ -145,13 +153,16 @@ __device__ __forceinline__ int map_request(const TopkMap m, int grow) {
   return 0;
 }
 
-// LDS of one workgroup.
-template <int NW, int CAP>
+// LDS of one workgroup of NW waves with a CAP-entry candidate list and WORDS-word position bitmaps.
+// A boundary bin of up to NW * 64 candidates (one per thread) is ranked pairwise.
+template <int NW, int CAP, int WORDS>
 struct TopkShared {
-  v2u cand[CAP + 1];                // candidates (code, position); bitmaps in the fallback;
-                                    // [CAP] absorbs appends past the end (the count still grows)
-  uint32_t hist[kBitmapWords];      // digit histogram, later per-word prefix popcounts
-  uint32_t bits[kBitmapWords];      // position bitmap
+  static constexpr int kWords = WORDS;
+  static constexpr int kBoundaryMax = NW * 64;
+  v2u cand[(CAP > WORDS ? CAP : WORDS) + 1];   // candidates (code, position); bitmaps in the fallback;
+                                               // [CAP] absorbs appends past the end (the count grows)
+  uint32_t hist[WORDS];             // digit histogram, later per-word prefix popcounts
+  uint32_t bits[WORDS];             // position bitmap
   uint32_t bk[kBoundaryMax];        // codes of the candidates in the boundary bin
   uint32_t bp[kBoundaryMax];        // and their positions
   uint32_t w0[NW];
@@ -167,9 +178,9 @@ struct TopkShared {
 // Bin of sh.hist[0, kBins) that holds the need-th largest element (1 <= need
 // <= total), with the number of elements in higher bins (above) and in the
 // bin itself (count).  Ends with a barrier.
-template <int THREADS, int CAP>
+template <int THREADS, typename Shared>
 __device__ __forceinline__ void pick_bin(uint32_t need, uint32_t& bin, uint32_t& above, uint32_t& count,
-                         TopkShared<THREADS / 64, CAP>& sh) {
+                         Shared& sh) {
   constexpr int NW = THREADS / 64;
   constexpr int DPT = kBins / THREADS;
   const int tid = threadIdx.x;
@@ -220,9 +231,9 @@ __device__ __forceinline__ void pick_bin(uint32_t need, uint32_t& bin, uint32_t&
 // largest.  With slack > 0 the search may stop once the bin holding the rank
 // has at most slack elements and return that bin's lowest code: then between
 // rank and rank + slack - 1 elements are >= the result (`need` is not set).
-template <int THREADS, int CAP, typename ForEach>
+template <int THREADS, typename Shared, typename ForEach>
 __device__ __forceinline__ uint32_t radix_select(ForEach for_each, uint32_t lo, uint32_t hi, uint32_t rank, uint32_t slack,
-                                 uint32_t& need, TopkShared<THREADS / 64, CAP>& sh) {
+                                 uint32_t& need, Shared& sh) {
   constexpr int DPT = kBins / THREADS;
   const int tid = threadIdx.x;
   need = rank;
@@ -242,7 +253,7 @@ __device__ __forceinline__ uint32_t radix_select(ForEach for_each, uint32_t lo, 
     });
     __syncthreads();
     uint32_t digit, above, count;
-    pick_bin<THREADS, CAP>(need, digit, above, count, sh);
+    pick_bin<THREADS>(need, digit, above, count, sh);
     need -= above;
     prefix |= digit << shift;
     pmask |= dmask << shift;
@@ -292,10 +303,10 @@ __device__ __forceinline__ void block_min_max_sum(uint32_t& mn, uint32_t& mx, ui
 }
 
 // Exclusive prefix popcounts of bitmap words [0, nwords) into pre[].
-template <int THREADS>
+template <int THREADS, int WORDS>
 __device__ __forceinline__ void bitmap_prefix(const uint32_t* bits, uint32_t* pre, int nwords, uint32_t* w) {
   constexpr int NW = THREADS / 64;
-  constexpr int WPT = (kBitmapWords + THREADS - 1) / THREADS;
+  constexpr int WPT = (WORDS + THREADS - 1) / THREADS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t local[WPT];
   uint32_t sum = 0u;
@@ -429,15 +440,15 @@ __device__ __forceinline__ void append_candidates(const uint32_t (&c)[UNR][VEC],
       }
 }
 
-template <int THREADS, int CAP, bool LEVEL0, bool FINAL, int VEC>
+template <int THREADS, int CAP, int SEG, bool LEVEL0, bool FINAL, int VEC>
 __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
   constexpr int NW = THREADS / 64;
   constexpr int UNR = kElemsPerPass / VEC;   // vectors per thread per pass
-  static_assert(kElemsPerPass <= 32, "a pass's candidate flags are one 32-bit mask per thread");
   static_assert(kBins % THREADS == 0, "bins per thread");
-  static_assert(CAP >= kBitmapWords, "fallback bitmaps reuse the candidate list");
-  static_assert(THREADS == kTopkThreads, "sample runs are one workgroup wide");
-  __shared__ TopkShared<NW, CAP> sh;
+  constexpr int WORDS = bitmap_words(SEG);
+  constexpr int kSampleSize = kSampleRuns * THREADS;   // sample runs are one workgroup wide
+  constexpr int kBoundaryMax = TopkShared<NW, CAP, WORDS>::kBoundaryMax;
+  __shared__ TopkShared<NW, CAP, WORDS> sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -554,7 +565,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
     const uint64_t want = ((uint64_t)kk * kSampleSize * 13u + 10ull * len - 1u) / (10ull * len) + 16u;
     if (ns > 0u && want < ns && want * (uint64_t)len <= (uint64_t)CAP * kSampleSize * 7u / 8u) {
       uint32_t unused;
-      T = radix_select<THREADS, CAP>(
+      T = radix_select<THREADS>(
           [&](auto&& visit) {
 #pragma unroll
             for (int b = 0; b < kSampleRuns; ++b)
@@ -657,7 +668,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
       }
       __syncthreads();
       uint32_t b, above, m;
-      pick_bin<THREADS, CAP>(kk, b, above, m, sh);
+      pick_bin<THREADS>(kk, b, above, m, sh);
       if (m <= (uint32_t)kBoundaryMax) {
         const uint32_t need = kk - above;   // taken from the boundary bin, 1 <= need <= m
         for (int ch = 0; ch < kChunks; ++ch) {
@@ -689,7 +700,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
         }
         __syncthreads();
         // ---- 5. output slots by position --------------------------------------
-        bitmap_prefix<THREADS>(sh.bits, sh.hist, nwords, sh.w0);
+        bitmap_prefix<THREADS, WORDS>(sh.bits, sh.hist, nwords, sh.w0);
         if (kChunks == 1) {
           // The list lives in registers now: stage the output row in its LDS
           // and store the row with coalesced writes.
@@ -763,7 +774,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
           cmax = max(cmax, sh.cand[i].x);
         }
         block_min_max_sum<NW>(cmin, cmax, unused, sh.w0, sh.w1, sh.w2);
-        tau = radix_select<THREADS, CAP>(
+        tau = radix_select<THREADS>(
             [&](auto&& visit) {
               for (uint32_t i = tid; i < C; i += THREADS) visit(sh.cand[i].x);
             },
@@ -778,7 +789,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
         for (uint32_t i = tid; i < C; i += THREADS)
           if (sh.cand[i].x == tau) atomicOr(&sh.bits[sh.cand[i].y >> 5], 1u << (sh.cand[i].y & 31));
         __syncthreads();
-        bitmap_prefix<THREADS>(sh.bits, sh.hist, nwords, sh.w0);
+        bitmap_prefix<THREADS, WORDS>(sh.bits, sh.hist, nwords, sh.w0);
         // ties past the first `need` by position drop out: code 0 is below tau
         for (uint32_t i = tid; i < C; i += THREADS)
           if (sh.cand[i].x == tau && bitmap_rank(sh.bits, sh.hist, sh.cand[i].y) >= need) sh.cand[i].x = 0u;
@@ -789,7 +800,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
       for (uint32_t i = tid; i < C; i += THREADS)
         if (sh.cand[i].x >= tau) atomicOr(&sh.bits[sh.cand[i].y >> 5], 1u << (sh.cand[i].y & 31));
       __syncthreads();
-      bitmap_prefix<THREADS>(sh.bits, sh.hist, nwords, sh.w0);
+      bitmap_prefix<THREADS, WORDS>(sh.bits, sh.hist, nwords, sh.w0);
       for (uint32_t i = tid; i < C; i += THREADS) {
         const v2u e = sh.cand[i];
         if (e.x >= tau) emit(bitmap_rank(sh.bits, sh.hist, e.y), e.y, e.x);
@@ -806,11 +817,11 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
     }
     if (kk > 0u) {
       uint32_t need;
-      const uint32_t tau = radix_select<THREADS, CAP>(
+      const uint32_t tau = radix_select<THREADS>(
           [&](auto&& visit) { stream([&](int, uint32_t code) { visit(code); }); }, 1u, 0xffffffffu, kk, 0u,
           need, sh);
       uint32_t* tie_bits = reinterpret_cast<uint32_t*>(sh.cand);   // the candidate list is free here
-      uint32_t* tie_pre = tie_bits + kBitmapWords;
+      uint32_t* tie_pre = tie_bits + WORDS;
       uint32_t eq = 0u;
       stream([&](int, uint32_t code) { eq += code == tau; });
       const uint32_t E = block_sum<NW>(eq, sh.w0);
@@ -822,7 +833,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
           if (code == tau) atomicOr(&tie_bits[pos >> 5], 1u << (pos & 31));
         });
         __syncthreads();
-        bitmap_prefix<THREADS>(tie_bits, tie_pre, nwords, sh.w0);
+        bitmap_prefix<THREADS, WORDS>(tie_bits, tie_pre, nwords, sh.w0);
       }
       auto selected = [&](int pos, uint32_t code) {
         return code > tau || (code == tau && (!rank_ties || bitmap_rank(tie_bits, tie_pre, pos) < need));
@@ -833,7 +844,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
         if (selected(pos, code)) atomicOr(&sh.bits[pos >> 5], 1u << (pos & 31));
       });
       __syncthreads();
-      bitmap_prefix<THREADS>(sh.bits, sh.hist, nwords, sh.w0);
+      bitmap_prefix<THREADS, WORDS>(sh.bits, sh.hist, nwords, sh.w0);
       stream([&](int pos, uint32_t code) {
         if (selected(pos, code)) emit(bitmap_rank(sh.bits, sh.hist, (uint32_t)pos), (uint32_t)pos, code);
       });
@@ -859,11 +870,22 @@ TopkPlan plan_topk(int32_t rows, int64_t width, int32_t k) {
   p.supported = true;
   p.buf_bytes[0] = p.buf_bytes[1] = 0;
   int64_t in_len = width > 0 ? width : 1;
+  const int64_t min_seg = std::max<int64_t>(8 * (int64_t)k, 16384);
+  // Few long rows (decode): one 512-thread workgroup takes a whole row of up to 131072 keys, twice the
+  // loads in flight of a 256-thread segment, in a single launch without a merge level.
+  if (rows > 0 && rows <= kWideRowsMax && in_len > min_seg && in_len <= kWideSeg && !topk_needs_big_cap(k)) {
+    TopkLevel& L = p.level[0];
+    L.in_len = in_len;
+    L.seg_len = (int32_t)in_len;
+    L.nseg = 1;
+    L.cfg = 2;
+    p.nlevels = 1;
+    return p;
+  }
   // few rows: split long windows so about this many workgroups run.  Every extra segment sends k
   // more candidates to the next level, so the target stays low: on 256 decode rows of up to 131072
   // keys, 2 segments per row ran 11% faster than 4.
   const int64_t target_wgs = 512;
-  const int64_t min_seg = std::max<int64_t>(8 * (int64_t)k, 16384);
   for (int lvl = 0; lvl < kMaxTopkLevels; ++lvl) {
     int64_t nseg = (in_len + kMaxSeg - 1) / kMaxSeg;
     if (lvl == 0 && in_len > min_seg && rows > 0 && rows < target_wgs) {
@@ -899,21 +921,22 @@ size_t topk_workspace_bytes(const TopkPlan& p) {
   return total;
 }
 
-template <int CAP, bool LEVEL0, bool FINAL>
+template <int THREADS, int CAP, int SEG, bool LEVEL0, bool FINAL>
 static void launch_vec(bool vec4, unsigned grid, const TopkKernelArgs& a, hipStream_t s) {
   if (vec4)
-    hipLaunchKernelGGL((topk_kernel<kTopkThreads, CAP, LEVEL0, FINAL, 4>), dim3(grid), dim3(kTopkThreads), 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<THREADS, CAP, SEG, LEVEL0, FINAL, 4>), dim3(grid), dim3(THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((topk_kernel<kTopkThreads, CAP, LEVEL0, FINAL, 1>), dim3(grid), dim3(kTopkThreads), 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<THREADS, CAP, SEG, LEVEL0, FINAL, 1>), dim3(grid), dim3(THREADS), 0, s, a);
 }
 
 template <int CAP>
 static void launch_cap(bool level0, bool final_level, bool vec4, unsigned grid, const TopkKernelArgs& a,
                        hipStream_t s) {
-  if (level0 && final_level) launch_vec<CAP, true, true>(vec4, grid, a, s);
-  else if (level0) launch_vec<CAP, true, false>(vec4, grid, a, s);
-  else if (final_level) launch_vec<CAP, false, true>(vec4, grid, a, s);
-  else launch_vec<CAP, false, false>(vec4, grid, a, s);
+  constexpr int kSeg = (int)kMaxSeg;
+  if (level0 && final_level) launch_vec<kTopkThreads, CAP, kSeg, true, true>(vec4, grid, a, s);
+  else if (level0) launch_vec<kTopkThreads, CAP, kSeg, true, false>(vec4, grid, a, s);
+  else if (final_level) launch_vec<kTopkThreads, CAP, kSeg, false, true>(vec4, grid, a, s);
+  else launch_vec<kTopkThreads, CAP, kSeg, false, false>(vec4, grid, a, s);
 }
 
 hipError_t launch_topk(const TopkArgs& ta, const TopkPlan& plan, void* ws, hipStream_t s) {
@@ -968,7 +991,8 @@ hipError_t launch_topk(const TopkArgs& ta, const TopkPlan& plan, void* ws, hipSt
     }
     const int64_t grid = (int64_t)ta.rows * L.nseg;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (L.cfg == 1) launch_cap<kBigCap>(level0, final_level, vec4, (unsigned)grid, a, s);
+    if (L.cfg == 2) launch_vec<kWideThreads, kSmallCap, (int)kWideSeg, true, true>(vec4, (unsigned)grid, a, s);
+    else if (L.cfg == 1) launch_cap<kBigCap>(level0, final_level, vec4, (unsigned)grid, a, s);
     else launch_cap<kSmallCap>(level0, final_level, vec4, (unsigned)grid, a, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

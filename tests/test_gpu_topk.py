@@ -39,7 +39,10 @@ def _run_topk(x, ks, ke, k, width=None, map_=None, row0=0):
 
 @pytest.mark.parametrize("kind", ["normal", "ties", "all_equal", "wide_range", "neg_inf_mix"])
 @pytest.mark.parametrize("rows,width,k", [(7, 300, 16), (40, 4096, 512), (3, 5000, 2048), (5, 70000, 100),
-                                          (2, 140000, 2048), (1200, 2000, 64)])
+                                          (2, 140000, 2048), (1200, 2000, 64),
+                                          # few long rows: one 512-thread workgroup per whole row
+                                          (48, 131072, 2048), (9, 131072, 2800), (512, 20000, 64),
+                                          (30, 16385, 2048)])
 def test_topk_exact(kind, rows, width, k):
     rng = np.random.default_rng(rows * 7 + width + k)
     x = _logits(rng, rows, width, kind)
@@ -127,7 +130,7 @@ def test_topk_large_k(kind, rows, width, k):
     assert_topk_exact(g, topk_indices(x, ks, ke, k), what=f"{kind} rows{rows} width{width} k{k}")
 
 
-@pytest.mark.parametrize("col0,ld", [(1, 1003), (3, 5003), (0, 5001)])
+@pytest.mark.parametrize("col0,ld", [(1, 1003), (3, 5003), (0, 5001), (1, 40003), (2, 131075)])
 def test_topk_unaligned_rows(col0, ld):
     # rows that do not start on 16 bytes take the 4-byte load path
     rng = np.random.default_rng(col0 + ld)
