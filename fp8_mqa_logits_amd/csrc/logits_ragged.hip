@@ -254,30 +254,42 @@ __global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogi
     const int boff0 = kl * kDim + (((2 * (lane >> 4)) ^ (kl & 7)) * 16);
     const int boff1 = kl * kDim + (((2 * (lane >> 4) + 1) ^ (kl & 7)) * 16);
 
+    // A tile's 64 key rows are 8 KiB contiguous in kv, so this thread's 16-byte chunk ci = tid + c2 *
+    // kThreads lies ci * 16 bytes from the tile's first key: a whole tile loads from one uniform base
+    // plus per-thread constant offsets, with no bounds checks.  Only a tile that runs past the last
+    // key clamps its key index to n - 1; those keys' logits are never stored (interior tiles end at or
+    // before every row's window end, edge tiles store only keys below tile_end <= n).
     v4i stage[kChunksPerThread];
     float stage_scale = 0.f;
     auto gload = [&](int tile) {
+      if (tile + kTileKeys <= n) {
+        const uint8_t* tb = a.kv + (size_t)tile * kDim;
 #pragma unroll
-      for (int c2 = 0; c2 < kChunksPerThread; ++c2) {
-        const int ci = tid + c2 * kThreads;
-        const int key = ci >> 3;
-        const int j = tile + key;
-        v4i v = {0, 0, 0, 0};
-        if (j < n) v = *reinterpret_cast<const v4i*>(a.kv + (size_t)j * kDim + (ci & 7) * 16);
-        stage[c2] = v;
-      }
-      if (tid < kTileKeys) {
-        const int j = tile + tid;
-        stage_scale = j < n ? a.kv_scale[j] : 0.f;
+        for (int c2 = 0; c2 < kChunksPerThread; ++c2)
+          stage[c2] = *reinterpret_cast<const v4i*>(tb + (tid + c2 * kThreads) * 16);
+        if (tid < kTileKeys) stage_scale = a.kv_scale[tile + tid];
+      } else {
+#pragma unroll
+        for (int c2 = 0; c2 < kChunksPerThread; ++c2) {
+          const int ci = tid + c2 * kThreads;
+          const int j = min(tile + (ci >> 3), n - 1);
+          stage[c2] = *reinterpret_cast<const v4i*>(a.kv + (size_t)j * kDim + (ci & 7) * 16);
+        }
+        if (tid < kTileKeys) stage_scale = a.kv_scale[min(tile + tid, n - 1)];
       }
     };
-    auto lstore = [&](int buf) {
+    // LDS offsets of this thread's chunks in a tile buffer (rows swizzled by key & 7), fixed per thread
+    int soff[kChunksPerThread];
 #pragma unroll
-      for (int c2 = 0; c2 < kChunksPerThread; ++c2) {
-        const int ci = tid + c2 * kThreads;
-        const int key = ci >> 3;
-        *reinterpret_cast<v4i*>(&s_kv[buf][key * kDim + (((ci & 7) ^ (key & 7)) * 16)]) = stage[c2];
-      }
+    for (int c2 = 0; c2 < kChunksPerThread; ++c2) {
+      const int ci = tid + c2 * kThreads;
+      const int key = ci >> 3;
+      soff[c2] = key * kDim + (((ci & 7) ^ (key & 7)) * 16);
+    }
+    auto lstore = [&](int buf) {
+      uint8_t* sb = &s_kv[buf][0];
+#pragma unroll
+      for (int c2 = 0; c2 < kChunksPerThread; ++c2) *reinterpret_cast<v4i*>(sb + soff[c2]) = stage[c2];
       if (tid < kTileKeys) s_scale[buf][tid] = stage_scale;
     };
 
