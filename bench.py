@@ -487,6 +487,13 @@ def run_workload(name, steps, warmup, cold=False, overlap=False):
     return res
 
 
+QUANT_SHAPES = (
+    ("kv_n65536_d128", 65536, 128),          # the 65536-key prefill's kv (per-token scales)
+    ("q_m8192_h32_d128", 8192 * 32, 128),    # its q, one row per (query row, head)
+    ("kv_n210000_d128", 210000, 128),        # the long-prefix workload's kv
+)
+
+
 def quant_workloads(steps, warmup):
     """Time indexer_quant_fp8 on the path's kv and q shapes: HBM bytes = 4 read + 1 written per
     element plus 4 per row (the scale), HIP events on the launch stream around each launch."""

@@ -264,6 +264,22 @@ def _paged() -> PagedInputs:
                         name="paged_decode_b64x4_ctx8k-128k")
 
 
+def _paged_sequential() -> PagedInputs:
+    """The decode workload with each request's pages physically consecutive (block table rows in
+    ascending page order instead of the random permutation): same lengths and work, used to measure
+    what the random page order costs the paged logits kernel."""
+    inp = paged_inputs(64, 4, 8192, 131072, 2048, seed=4, page_size=64,
+                       name="paged_decode_b64x4_ctx8k-128k_sequential_pages")
+    pages = (inp.ctx.astype(np.int64) + 63) // 64
+    bt = np.full_like(inp.block_table, -1)
+    off = 0
+    for b in range(inp.B):
+        bt[b, :pages[b]] = np.arange(off, off + pages[b], dtype=np.int32)
+        off += int(pages[b])
+    inp.block_table = bt
+    return inp
+
+
 def _long210k() -> RaggedInputs:
     # warm_long_150K+60K: prefix 150000, extend 60000 -> m = 7500, n = 210000
     return ragged_inputs(7500, 210000, 2048, seed=5, name="prefill_m7500_n210000_cap2GB",
@@ -275,6 +291,7 @@ CONFIGS: Dict[str, Callable[[], object]] = {
     "prefill_64k": _cold64k,
     "prefill_35k": _square35k,
     "paged_decode": _paged,
+    "paged_decode_sequential": _paged_sequential,
     "long_prefix_210k": _long210k,
 }
 
