@@ -27,6 +27,9 @@ Extra modes (used to collect counters and cross-checks):
   --no-cpu-baseline    skip the oracle timing (profiling runs)
   --copy-calibration   only run a plain device copy of known size (for
                        scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+  --core-probe N       only run the logits-core probe (the logits kernels'
+                       per-fragment code on register operands) N times at the
+                       ragged kernel's occupancy (for its SQ counters)
   --all-workloads PATH time every workload, with the oracle beside each,
                        and write a JSON list to PATH
   --trace-summary CSV  (no GPU) summarise a rocprofv3 kernel_trace.csv or
@@ -77,6 +80,8 @@ def _args():
                     help="rewrite a 512 MiB scratch buffer before each timed step (cold caches)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--core-probe", type=int, default=0, metavar="LAUNCHES",
+                    help="only run the logits-core probe at the ragged kernel's occupancy, LAUNCHES times")
     ap.add_argument("--trace-summary", default="", metavar="CSV")
     ap.add_argument("--all-workloads", default="")
     ap.add_argument("--overlap", action="store_true", help="time the fused loop serial vs overlapped")
@@ -349,6 +354,7 @@ def measured_peaks():
         t = flops / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
         if t > mfma_tflops:
             mfma_tflops, best = t, blocks
+    core = core_probe(cus, (2, 3, 4), iters=2048, reps=reps)
     nbytes = 1 << 30
     x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
     y = torch.empty_like(x)
@@ -363,8 +369,35 @@ def measured_peaks():
     del x, y, out
     torch.cuda.empty_cache()
     return {"mfma_fp8_tflops": round(mfma_tflops, 1), "copy_gbps": round(copy_gbps, 1),
+            "logits_core_tflops": {str(k): round(v, 1) for k, v in core.items()},
             "mfma_probe": f"{best} x 256 threads, 4 x {iters} fp8 16x16x128 MFMAs per wave, {reps} launches",
+            "logits_core_probe": (f"2, 3 and 4 x {cus} workgroups of 256 threads, 2048 logits-core fragments "
+                                  f"(8 fp8 16x16x128 MFMAs + exact epilogue) per wave, {reps} launches"),
             "copy_probe": f"1 GiB device copy, read + written bytes, {reps} copies"}
+
+
+# Workgroups of the ragged logits kernel resident per CU (4 waves each, 168 VGPRs: 3 waves per SIMD).
+RAGGED_WGS_PER_CU = 3
+
+
+def core_probe(cus, per_cu_list, iters, reps):
+    """TFLOP/s of the logits-core probe (the logits kernels' per-fragment MFMA + exact-epilogue code on
+    register operands, no memory traffic) at each number of 256-thread workgroups per CU."""
+    import torch
+    import fp8_mqa_logits_amd as F
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for per_cu in per_cu_list:
+        blocks = per_cu * cus
+        out, flops = F.fp8idx_probe_logits_core(blocks, iters)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            F.fp8idx_probe_logits_core(blocks, iters, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        res[per_cu] = flops / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
+    return res
 
 
 def _time_fused(step, steps, warmup, overlap=False, cold=False):
@@ -667,6 +700,7 @@ def prep_workloads(steps, warmup):
 
 def copy_calibration():
     import torch
+    core = core_probe(cus, (2, 3, 4), iters=2048, reps=reps)
     nbytes = 1 << 30
     x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
     y = torch.empty_like(x)
@@ -755,6 +789,12 @@ def main():
     F.load_library()
     if a.copy_calibration:
         copy_calibration()
+        return
+    if a.core_probe:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        t = core_probe(cus, (RAGGED_WGS_PER_CU,), iters=4096, reps=a.core_probe)[RAGGED_WGS_PER_CU]
+        print(json.dumps({"probe": "logits_core", "wgs_per_cu": RAGGED_WGS_PER_CU, "launches": a.core_probe,
+                          "tflops": round(t, 1)}), flush=True)
         return
     if a.all_workloads:
         rows = []
@@ -869,6 +909,8 @@ def main():
             pk["logits_frac_of_copy"] = round(roof["achieved"] / pk["copy_gbps"], 4)
         else:
             pk["logits_frac_of_mfma_probe"] = round(roof["achieved"] / pk["mfma_fp8_tflops"], 4)
+            pk["logits_frac_of_core_probe"] = round(
+                roof["achieved"] / pk["logits_core_tflops"][str(RAGGED_WGS_PER_CU)], 4)
         out["measured_peaks"] = pk
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(inp, a.cpu_seconds)

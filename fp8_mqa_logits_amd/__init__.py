@@ -44,4 +44,5 @@ from .binding import (  # noqa: F401
     fp8idx_rows_per_chunk,
     fp8idx_version,
     fp8idx_probe_mfma_fp8,
+    fp8idx_probe_logits_core,
 )

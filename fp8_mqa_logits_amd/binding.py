@@ -39,7 +39,7 @@ EXPORTED = (
     "fp8idx_status_string", "fp8idx_last_hip_error", "fp8idx_version",
     "indexer_quant_fp8", "indexer_logits_topk_ragged_overlap",
     "indexer_prepare_ragged", "indexer_prepare_decode",
-    "indexer_sparse_mla", "fp8idx_sparse_mla_workspace_bytes", "fp8idx_probe_mfma_fp8",
+    "indexer_sparse_mla", "fp8idx_sparse_mla_workspace_bytes", "fp8idx_probe_mfma_fp8", "fp8idx_probe_logits_core",
     "fp8idx_validate_only", "indexer_logits_ragged_noalloc",
 )
 
@@ -128,6 +128,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       _P, _P, _P, _SZ, _P]),
         "fp8idx_sparse_mla_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
         "fp8idx_probe_mfma_fp8": (_I32, [_I32, _I32, _P, ctypes.POINTER(ctypes.c_double), _P]),
+        "fp8idx_probe_logits_core": (_I32, [_I32, _I32, _P, ctypes.POINTER(ctypes.c_double), _P]),
         "fp8idx_validate_only": (_I32, [_I32, ctypes.POINTER(CallArgs)]),
         "indexer_logits_ragged_noalloc": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _I64, _I32,
                                                  _P]),
@@ -538,12 +539,7 @@ def indexer_logits_topk_paged(q, kv_pool, scale_pool, weights, row_len, block_ta
     return out
 
 
-def fp8idx_probe_mfma_fp8(blocks: int, iters: int, *, out: Optional[torch.Tensor] = None, stream=None):
-    """Launch the fp8 MFMA throughput probe (a measurement helper, not an indexer step).
-
-    Returns (out, flops): out is the float32 [blocks * 256] sink the kernel writes, flops the
-    launch's MFMA flops.  The caller times the launch (events on `stream`).
-    """
+def _probe(name: str, blocks: int, iters: int, out: Optional[torch.Tensor], stream):
     dev = torch.device("cuda", torch.cuda.current_device())
     if out is None:
         out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
@@ -554,9 +550,27 @@ def fp8idx_probe_mfma_fp8(blocks: int, iters: int, *, out: Optional[torch.Tensor
     flops = ctypes.c_double(0.0)
     L = load_library()
     with torch.cuda.device(dev):
-        st = L.fp8idx_probe_mfma_fp8(int(blocks), int(iters), _ptr(out), ctypes.byref(flops), _stream(dev, stream))
-    _check("fp8idx_probe_mfma_fp8", st)
+        st = getattr(L, name)(int(blocks), int(iters), _ptr(out), ctypes.byref(flops), _stream(dev, stream))
+    _check(name, st)
     return out, flops.value
+
+
+def fp8idx_probe_mfma_fp8(blocks: int, iters: int, *, out: Optional[torch.Tensor] = None, stream=None):
+    """Launch the fp8 MFMA throughput probe (a measurement helper, not an indexer step).
+
+    Returns (out, flops): out is the float32 [blocks * 256] sink the kernel writes, flops the
+    launch's MFMA flops.  The caller times the launch (events on `stream`).
+    """
+    return _probe("fp8idx_probe_mfma_fp8", blocks, iters, out, stream)
+
+
+def fp8idx_probe_logits_core(blocks: int, iters: int, *, out: Optional[torch.Tensor] = None, stream=None):
+    """Launch the logits-core probe: the logits kernels' per-fragment MFMA + exact-epilogue code on
+    register operands, no memory traffic (a measurement helper, not an indexer step).
+
+    Returns (out, flops) like fp8idx_probe_mfma_fp8; the caller times the launch.
+    """
+    return _probe("fp8idx_probe_logits_core", blocks, iters, out, stream)
 
 
 def indexer_quant_fp8(x, *, codes: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,

@@ -42,8 +42,11 @@ HIP_FLAGS = [
 # wave is carried from step to step; in the default AGPR form the compiler gave each value MFMA a
 # destination other than its accumulator input and copied all 128 output registers through VGPRs
 # in every step, which the VGPR form avoids (the kernel runs one wave per SIMD and has the room).
+# peak_probe.hip: the same form, which the logits kernels get by themselves (their register pressure
+# leaves no room for AGPR copies), so that the logits-core probe runs their instruction mix.
 FILE_FLAGS = {
     "sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "peak_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

@@ -185,5 +185,8 @@ hipError_t launch_sparse_mla(const SparseMlaArgs& a, const SparseMlaPlan& plan, 
 constexpr int kProbeChains = 4;
 constexpr int kProbeThreads = 256;
 hipError_t launch_mfma_probe(int blocks, int iters, float* out, hipStream_t s);
+// Logits-core probe: blocks x kProbeThreads threads, each wave iters x (8 MFMAs + the exact
+// epilogue of one 16-key fragment) on register operands; one float per thread to out.
+hipError_t launch_logits_core_probe(int blocks, int iters, float* out, hipStream_t s);
 
 }  // namespace fp8idx

@@ -467,6 +467,22 @@ FP8IDX_API int32_t fp8idx_rows_per_chunk(size_t logits_cap_bytes, int64_t width,
 FP8IDX_API fp8idx_status fp8idx_probe_mfma_fp8(int32_t blocks, int32_t iters, float* out, double* flops,
                                                void* stream);
 
+/*
+ * Measurement helper, not a step of the indexer: the logits kernels' per-fragment
+ * core without memory traffic.  Launches `blocks` workgroups of 256 threads;
+ * each wave runs iters x one 16-key fragment of the logits core (eight
+ * v_mfma_f32_16x16x128_f8f6f4 for 4 query rows x 32 heads, then ReLU, the head
+ * weights and the cross-lane head reduction, the same code as the logits
+ * kernels) on register operands.  With as many workgroups per CU as the ragged
+ * logits kernel keeps resident, its rate is the issue-bound ceiling of that
+ * kernel.  out: device float32 [blocks * 256], written (keeps the work live;
+ * its value means nothing).  *flops (if non-NULL) receives blocks * 4 waves *
+ * iters * 8 * 65536.  blocks > 0 and iters > 0, else FP8IDX_EINVAL.
+ * Allocates nothing; runs on `stream`; the caller times it.
+ */
+FP8IDX_API fp8idx_status fp8idx_probe_logits_core(int32_t blocks, int32_t iters, float* out, double* flops,
+                                                  void* stream);
+
 /* Static string naming a status. */
 FP8IDX_API const char* fp8idx_status_string(int32_t status);
 

@@ -34,7 +34,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(binding.EXPORTED) == names
@@ -289,3 +289,13 @@ def test_mfma_probe_validation(lib):
     assert lib.fp8idx_probe_mfma_fp8(4, 8, NULL, ctypes.byref(flops), NULL) == EINVAL
     assert lib.fp8idx_probe_mfma_fp8(4, 8, P + 2, ctypes.byref(flops), NULL) == EINVAL
     assert lib.fp8idx_probe_mfma_fp8(4, 8, P, ctypes.byref(flops), NULL) == EDEV
+
+
+def test_logits_core_probe_validation(lib):
+    flops = ctypes.c_double(0.0)
+    f = lib.fp8idx_probe_logits_core
+    assert f(0, 8, P, ctypes.byref(flops), NULL) == EINVAL
+    assert f(4, 0, P, ctypes.byref(flops), NULL) == EINVAL
+    assert f(4, 8, NULL, ctypes.byref(flops), NULL) == EINVAL
+    assert f(4, 8, P + 2, ctypes.byref(flops), NULL) == EINVAL
+    assert f(4, 8, P, ctypes.byref(flops), NULL) == EDEV
