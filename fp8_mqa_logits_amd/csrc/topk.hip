@@ -40,7 +40,7 @@
 // Few long rows (at most 512 rows of at most 131072 keys, k up to about
 // 2800: paged decode) take one 512-thread workgroup per whole row instead:
 // twice the loads in flight of a 256-thread segment, a single launch and no
-// merge level (position bitmaps sized for 131072 keys, two workgroups per CU).
+// merge level (position bitmaps sized for 131072 keys, one workgroup per CU).
 // Other rows longer than one segment, or few rows that need more parallelism, are
 // split: each segment emits its local top-k (code, index) pairs in index
 // order, and further levels of the same kernel select from the concatenated

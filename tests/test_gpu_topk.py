@@ -22,6 +22,9 @@ def _logits(rng, rows, width, kind):
         x = np.full((rows, width), 3.5, np.float32)
     elif kind == "wide_range":
         x = (rng.standard_normal((rows, width)) * np.exp(rng.uniform(-30, 30, (rows, width)))).astype(np.float32)
+    elif kind == "trend":
+        # rising along the row: the top keys crowd into the last part of a long row
+        x = (np.arange(width, dtype=np.float64)[None, :] * 1e-3 + rng.standard_normal((rows, width))).astype(np.float32)
     elif kind == "neg_inf_mix":
         x = (rng.standard_normal((rows, width))).astype(np.float32)
         x[rng.random((rows, width)) < 0.3] = -np.inf
@@ -143,3 +146,35 @@ def test_topk_unaligned_rows(col0, ld):
     torch.cuda.synchronize()
     e = topk_indices(base[:, col0:col0 + width], ks, ke, k)
     assert_topk_exact(g.cpu().numpy(), e, what=f"col0 {col0} ld {ld}")
+
+
+@pytest.mark.parametrize("kind", ["normal", "trend", "ties", "wide_range", "neg_inf_mix"])
+def test_topk_long_rows_value_mixes(kind):
+    """Few long rows (the one-workgroup-per-row path) over value distributions that stress the sampled
+    threshold: rising along the row (trend), heavy ties, a huge dynamic range and -inf runs.  Window
+    lengths range from under k to the full 131072 keys at unaligned starts; three calls on two inputs
+    share one workspace."""
+    rng = np.random.default_rng(4242)
+    rows, width, k = 64, 131072, 2048
+    x = _logits(rng, rows, width, kind)
+    lens = np.array([32768, 32769, 65536, 65537, 98304, 98305, 131072, 1000, 2048, 40000, 131071, 100003]
+                    * 6)[:rows - 4]
+    lens = np.concatenate([lens, rng.integers(2049, width + 1, 4)])
+    ks = np.array([int(rng.integers(0, width - l + 1)) for l in lens], np.int32)
+    ke = (ks + lens).astype(np.int32)
+    need = F.fp8idx_workspace_bytes(F.OP_TOPK, rows, width, k, 0)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    # a second input through the same workspace
+    x2 = x[::-1].copy() if kind != "trend" else x[:, ::-1].copy()
+    xd, x2d, ksd, ked = to_dev(x), to_dev(x2), to_dev(ks), to_dev(ke)
+    g1 = F.indexer_topk(xd, ked, k, ks=ksd, workspace=ws)
+    g2 = F.indexer_topk(x2d, ked, k, ks=ksd, workspace=ws)
+    g3 = F.indexer_topk(xd, ked, k, ks=ksd, workspace=ws)
+    torch.cuda.synchronize()
+    assert_topk_exact(g1.cpu().numpy(), topk_indices(x, ks, ke, k), what=f"long rows {kind}")
+    assert_topk_exact(g2.cpu().numpy(), topk_indices(x2, ks, ke, k), what=f"long rows {kind}, second input")
+    assert torch.equal(g1, g3)
+    for g in (g1.cpu().numpy(), g2.cpu().numpy()):
+        for r in range(rows):
+            sel = g[r][g[r] >= 0]
+            assert np.all(np.diff(sel) > 0)
