@@ -631,9 +631,11 @@ fp8idx_status indexer_logits_topk_ragged_overlap(const uint8_t* q, const uint8_t
     const int b = ci & 1;
     // the top-k of chunk ci - 2 must have read this buffer before it is rewritten
     if (ci >= 2 && (e = hipStreamWaitEvent(main_st, ev[2 + b], 0)) != hipSuccess) return hip_fail(e);
-    // the logits launches all run on the main stream, one after another, so they share one counter set
+    // the logits launches all run on the main stream, one after another, so they share one counter set;
+    // after the first chunk, one workgroup slot per CU is left to the previous chunk's top-k
     fp8idx::RaggedLogitsArgs la{q + (size_t)s0 * fp8idx::kQRowBytesHost, kv, kv_scale,
-                                weights + (size_t)s0 * 32, ks + s0, ke + s0, rows, n, bufs[b], ld, 0, queue};
+                                weights + (size_t)s0 * 32, ks + s0, ke + s0, rows, n, bufs[b], ld, 0, queue,
+                                ci > 0 ? std::max(1, dev.ragged_wgs_per_cu - 1) : 0};
     if ((e = fp8idx::launch_logits_ragged(la, dev, main_st)) != hipSuccess) return hip_fail(e);
     if ((e = hipEventRecord(ev[b], main_st)) != hipSuccess) return hip_fail(e);
     if ((e = hipStreamWaitEvent(side, ev[b], 0)) != hipSuccess) return hip_fail(e);

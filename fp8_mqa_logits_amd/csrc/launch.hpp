@@ -20,6 +20,8 @@ struct RaggedLogitsArgs {
   int64_t ld;
   int32_t clean;
   unsigned int* queue;   // kRaggedQueueWords work-queue counters (device), cleared by each launch
+  int32_t wgs_per_cu;    // resident workgroups to launch per CU; 0: as many as fit (leaves none for
+                         // kernels on other streams)
 };
 
 // Work-queue counters of one ragged logits launch: one claim counter per XCD queue, padded to

@@ -371,7 +371,8 @@ hipError_t launch_logits_ragged(const RaggedLogitsArgs& a, const DeviceInfo& dev
   if (a.m <= 0) return hipSuccess;
   const int64_t row_blocks = (a.m + kRowsPerItem - 1) / kRowsPerItem;
   // resident workgroups of this kernel on the whole device, rounded to XCDs
-  const int per_cu = dev.ragged_wgs_per_cu > 0 ? dev.ragged_wgs_per_cu : 1;
+  int per_cu = dev.ragged_wgs_per_cu > 0 ? dev.ragged_wgs_per_cu : 1;
+  if (a.wgs_per_cu > 0) per_cu = std::min(per_cu, (int)a.wgs_per_cu);
   int64_t resident = (int64_t)(dev.cu_count > 0 ? dev.cu_count : 256) * per_cu;
   if (resident >= 8) resident = resident / 8 * 8;
   // key splits: multiples of 8 (one queue per XCD), doubled until there are
