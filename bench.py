@@ -112,7 +112,10 @@ class RaggedStep:
             _dev(inp.q), _dev(inp.kv), _dev(inp.kv_scale), _dev(inp.weights), _dev(inp.ks), _dev(inp.ke))
         m, n, k = inp.m, inp.n, inp.k
         self.cap = inp.cap_bytes
-        self.rpc = F.fp8idx_rows_per_chunk(self.cap, n, m)
+        # the fused entry's chunks: ceil(m / the cap-derived size), rows spread evenly over them
+        cmax = F.fp8idx_rows_per_chunk(self.cap, n, m)
+        nch = -(-m // cmax)
+        self.rpc = -(-m // nch)
         self.ld = (n + 3) // 4 * 4
         self.logits = torch.empty((self.rpc, self.ld), dtype=torch.float32, device="cuda")
         tk = F.fp8idx_workspace_bytes(F.OP_TOPK, self.rpc, n, k, 0)

@@ -169,6 +169,12 @@ FusedLayout fused_layout(int32_t rows, int64_t width, int32_t k, size_t cap, int
   if (granule > 1 && rpc < rows) rpc = std::max<int32_t>(granule, rpc / granule * granule);
   rpc = std::min(rpc, rows);
   if (rpc <= 0) return L;
+  // As many chunks as the cap-derived size gives, with the rows spread evenly over them (in whole
+  // granules): a short last chunk would run its launches at a fraction of their rate.
+  const int32_t nch = (rows + rpc - 1) / rpc;
+  int32_t even = (rows + nch - 1) / nch;
+  if (granule > 1) even = (even + granule - 1) / granule * granule;
+  rpc = std::min(rpc, even);
   const int32_t last = rows % rpc == 0 ? rpc : rows % rpc;
   const fp8idx::TopkPlan p0 = fp8idx::plan_topk(rpc, width, k);
   const fp8idx::TopkPlan p1 = fp8idx::plan_topk(last, width, k);

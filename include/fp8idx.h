@@ -209,7 +209,9 @@ FP8IDX_API fp8idx_status indexer_topk(const float* logits, int64_t ld, int32_t r
 
 /*
  * Fused ragged logits + top-k under a logits byte cap (the row-chunked loop
- * of the chunking page: rows per chunk = max(1, floor(cap / (n * 4)))).  Per
+ * of the chunking page: at most fp8idx_rows_per_chunk rows per chunk, i.e.
+ * max(1, floor(cap / (n * 4)))).  The rows are spread evenly over that many
+ * chunks, ceil(m / fp8idx_rows_per_chunk), so the last one is not short.  Per
  * chunk: logits into the workspace, then top-k into `out`, on one stream.
  * The full rows x n buffer is never materialised unless the cap allows it.
  *
@@ -262,7 +264,7 @@ FP8IDX_API fp8idx_status indexer_logits_topk_ragged_overlap(const uint8_t* q, co
  * (block_table[b, j / 64] * 64 + j % 64) when map_to_slots != 0, else raw key
  * positions j.  `width` bounds every row length (the logits row stride used in
  * the workspace).  Requests are chunked so that at most logits_cap_bytes of
- * logits exist at once (0 = all rows at once).
+ * logits exist at once (0 = all rows at once), spread evenly over the chunks.
  *   ws_bytes >= fp8idx_workspace_bytes_paged(B, next_n, width, k, logits_cap_bytes)
  * Chunks hold whole requests: at least one request per chunk even when one
  * request's next_n rows exceed the cap.
@@ -447,9 +449,11 @@ FP8IDX_API size_t fp8idx_workspace_bytes(int32_t op, int32_t rows, int64_t width
 FP8IDX_API size_t fp8idx_workspace_bytes_paged(int32_t B, int32_t next_n, int32_t width, int32_t k,
                                     size_t logits_cap_bytes);
 
-/* Rows per chunk of the fused ragged entry: max(1, floor(cap / (ld * 4))),
+/* Largest chunk of the fused ragged entry: max(1, floor(cap / (ld * 4))),
  * capped at rows, where ld = width rounded up to a multiple of 4 (the row
- * stride of the workspace logits); cap 0 gives rows.  Pure host arithmetic. */
+ * stride of the workspace logits); cap 0 gives rows.  The entry runs
+ * ceil(rows / this) chunks of ceil(rows / chunks) rows (the last one takes the
+ * remainder).  Pure host arithmetic. */
 FP8IDX_API int32_t fp8idx_rows_per_chunk(size_t logits_cap_bytes, int64_t width, int32_t rows);
 
 /*

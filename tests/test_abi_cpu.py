@@ -170,8 +170,9 @@ def test_rows_per_chunk_follows_chunking_page(lib):
 def test_fused_workspace_covers_chunk_and_candidates(lib):
     cap = 2_000_000_000
     ws = F.fp8idx_workspace_bytes(F.OP_LOGITS_TOPK_RAGGED, 7500, 210000, 2048, cap)
-    logits = 2380 * 210000 * 4
-    cand = 2380 * 4 * 2048 * 8          # 4 segments of up to 52500 keys per row
+    # the cap allows 2380 rows per chunk: 4 chunks, so 1875 rows each
+    logits = 1875 * 210000 * 4
+    cand = 1875 * 4 * 2048 * 8          # 4 segments of up to 52500 keys per row
     assert ws >= logits + cand
     assert ws <= logits + cand + 4096
     # one-shot on 8192 x 65536: the work-queue counters and the full 2 GiB buffer, single-segment top-k

@@ -89,7 +89,8 @@ def test_full_size_ragged_configs_sampled(name):
     cap = inp.cap_bytes
     out = F.indexer_logits_topk_ragged(*d, inp.k, logits_cap_bytes=cap)
     torch.cuda.synchronize()
-    chunk = F.fp8idx_rows_per_chunk(cap, inp.n, inp.m)
+    cmax = F.fp8idx_rows_per_chunk(cap, inp.n, inp.m)
+    chunk = -(-inp.m // -(-inp.m // cmax))   # the entry's chunks: the rows spread evenly over ceil(m / cmax)
     rows = _sample_rows(inp.m, chunk if cap else 0)
     ridx = np.array(rows)
     # the sampled rows' logits from the same kernel (values do not depend on batching)
