@@ -703,7 +703,6 @@ def prep_workloads(steps, warmup):
 
 def copy_calibration():
     import torch
-    core = core_probe(cus, (2, 3, 4), iters=2048, reps=reps)
     nbytes = 1 << 30
     x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
     y = torch.empty_like(x)
