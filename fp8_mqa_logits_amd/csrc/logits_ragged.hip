@@ -29,7 +29,7 @@
 //   items cover every queue (small problems) neither the clear nor any
 //   atomic runs.  Two launches that may run at the same time must therefore
 //   be given different counter buffers.
-// - Keys stream through LDS in tiles of 64 keys x 128 bytes (8 KiB, double
+// - Keys stream through LDS in tiles of 128 keys x 128 bytes (16 KiB, double
 //   buffered), loaded with coalesced 16-byte global loads.  Inside a row the
 //   16-byte chunks are XOR-swizzled by (key & 7) so that the B-operand reads
 //   (lane l: key l % 16, bytes 32 * (l / 16) .. +32) hit distinct banks.
@@ -54,7 +54,7 @@
 
 namespace fp8idx {
 
-constexpr int kTileKeys = 64;
+constexpr int kTileKeys = 128;
 constexpr int kWaves = 4;
 constexpr int kRowsPerItem = 4 * kWaves;
 
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogi
     const int boff0 = kl * kDim + (((2 * (lane >> 4)) ^ (kl & 7)) * 16);
     const int boff1 = kl * kDim + (((2 * (lane >> 4) + 1) ^ (kl & 7)) * 16);
 
-    // A tile's 64 key rows are 8 KiB contiguous in kv, so this thread's 16-byte chunk ci = tid + c2 *
+    // A tile's 128 key rows are 16 KiB contiguous in kv, so this thread's 16-byte chunk ci = tid + c2 *
     // kThreads lies ci * 16 bytes from the tile's first key: a whole tile loads from one uniform base
     // plus per-thread constant offsets, with no bounds checks.  Only a tile that runs past the last
     // key clamps its key index to n - 1; those keys' logits are never stored (interior tiles end at or
@@ -376,7 +376,7 @@ hipError_t launch_logits_ragged(const RaggedLogitsArgs& a, const DeviceInfo& dev
   int64_t resident = (int64_t)(dev.cu_count > 0 ? dev.cu_count : 256) * per_cu;
   if (resident >= 8) resident = resident / 8 * 8;
   // key splits: multiples of 8 (one queue per XCD), doubled until there are
-  // about 8 items per resident workgroup, keeping >= 128 keys (2 tiles) per split
+  // about 8 items per resident workgroup, keeping >= 128 keys (1 tile) per split
   const int64_t max_splits = std::max<int64_t>(1, a.n / 128);
   int64_t splits = std::min<int64_t>(8, max_splits);
   while (splits * 2 <= max_splits && row_blocks * splits < 8 * resident) splits *= 2;
