@@ -30,9 +30,12 @@
 //   atomic runs.  Two launches that may run at the same time must therefore
 //   be given different counter buffers.
 // - Keys stream through LDS in tiles of 128 keys x 128 bytes (16 KiB, double
-//   buffered), loaded with coalesced 16-byte global loads.  Inside a row the
+//   buffered), loaded by 16-byte LDS-DMA loads (global_load_lds_dwordx4: no
+//   staging registers, each instruction a coalesced 1 KiB).  Inside a row the
 //   16-byte chunks are XOR-swizzled by (key & 7) so that the B-operand reads
-//   (lane l: key l % 16, bytes 32 * (l / 16) .. +32) hit distinct banks.
+//   (lane l: key l % 16, bytes 32 * (l / 16) .. +32) hit distinct banks.  A
+//   tile's logits are stored after the next tile's barrier, so the wait for
+//   each tile's loads before that barrier never waits on fresh stores.
 // - Per 16-key fragment a wave issues 8 MFMAs (4 rows x 2 head tiles of 16);
 //   each lane then holds 8 heads of one (row, key) score set.  ReLU and the
 //   head weights are applied in registers (max + fma per score), the four
@@ -140,12 +143,17 @@ __global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogi
                                                                        int use_queue) {
   constexpr int kThreads = 64 * WAVES;
   constexpr int kRows = 4 * WAVES;
-  constexpr int kChunks = kTileKeys * (kDim / 16);   // 16-byte chunks per tile
-  constexpr int kChunksPerThread = kChunks / kThreads;
-  static_assert(kChunks % kThreads == 0, "tile chunks must divide the workgroup");
+  constexpr int kFrags = kTileKeys / 16;                           // 16-key MFMA fragments per tile
+  constexpr int kDmaPerWave = kTileKeys * kDim / (1024 * WAVES);   // 1 KiB LDS-DMA blocks per wave per tile
+  static_assert(kTileKeys * kDim % (1024 * WAVES) == 0, "tile blocks must divide the workgroup");
+  static_assert(kTileKeys % 64 == 0, "scales load 64 per instruction");
 
-  __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][kTileKeys * kDim];
-  __shared__ float s_scale[2][kTileKeys];
+  // Two tile buffers as separate arrays, so the compiler can tell the buffer being read from the one
+  // being filled and puts no wait for the fill before the reads.
+  __shared__ __attribute__((aligned(16))) uint8_t s_kv0[kTileKeys * kDim];
+  __shared__ __attribute__((aligned(16))) uint8_t s_kv1[kTileKeys * kDim];
+  __shared__ __attribute__((aligned(16))) float s_sc0[kTileKeys];
+  __shared__ __attribute__((aligned(16))) float s_sc1[kTileKeys];
   __shared__ int s_ks[kRows];
   __shared__ int s_ke[kRows];
   __shared__ unsigned int s_claim;
@@ -254,82 +262,78 @@ __global__ __launch_bounds__(64 * WAVES, 3) void logits_ragged_kernel(RaggedLogi
     const int boff0 = kl * kDim + (((2 * (lane >> 4)) ^ (kl & 7)) * 16);
     const int boff1 = kl * kDim + (((2 * (lane >> 4) + 1) ^ (kl & 7)) * 16);
 
-    // A tile's 128 key rows are 16 KiB contiguous in kv, so this thread's 16-byte chunk ci = tid + c2 *
-    // kThreads lies ci * 16 bytes from the tile's first key: a whole tile loads from one uniform base
-    // plus per-thread constant offsets, with no bounds checks.  Only a tile that runs past the last
-    // key clamps its key index to n - 1; those keys' logits are never stored (interior tiles end at or
-    // before every row's window end, edge tiles store only keys below tile_end <= n).
-    v4i stage[kChunksPerThread];
-    float stage_scale = 0.f;
-    auto gload = [&](int tile) {
-      if (tile + kTileKeys <= n) {
-        const uint8_t* tb = a.kv + (size_t)tile * kDim;
+    // Tiles go from kv straight into LDS (16-byte LDS-DMA loads, no staging registers).  Lane l of
+    // DMA block b (keys 8b .. 8b + 7 of the tile, 1 KiB) fills LDS bytes 1024 b + 16 l: key 8b + l / 8,
+    // slot l % 8, which holds that key's 16-byte chunk (l % 8) ^ (key & 7) = (l % 8) ^ (l / 8), the
+    // swizzle the B-operand reads expect.  Keys past the last one are clamped to n - 1; their logits
+    // are never stored (interior tiles end at or before every row's window end, edge tiles store only
+    // keys below tile_end <= n).
+    const int dma_key = lane >> 3;
+    const int dma_chunk = (lane & 7) ^ (lane >> 3);
+    auto dma = [&](int tile, uint8_t* skv, float* ssc) {
 #pragma unroll
-        for (int c2 = 0; c2 < kChunksPerThread; ++c2)
-          stage[c2] = *reinterpret_cast<const v4i*>(tb + (tid + c2 * kThreads) * 16);
-        if (tid < kTileKeys) stage_scale = a.kv_scale[tile + tid];
-      } else {
-#pragma unroll
-        for (int c2 = 0; c2 < kChunksPerThread; ++c2) {
-          const int ci = tid + c2 * kThreads;
-          const int j = min(tile + (ci >> 3), n - 1);
-          stage[c2] = *reinterpret_cast<const v4i*>(a.kv + (size_t)j * kDim + (ci & 7) * 16);
-        }
-        if (tid < kTileKeys) stage_scale = a.kv_scale[min(tile + tid, n - 1)];
+      for (int i = 0; i < kDmaPerWave; ++i) {
+        const int blk = wave * kDmaPerWave + i;
+        const int key = min(tile + 8 * blk + dma_key, n - 1);
+        __builtin_amdgcn_global_load_lds(a.kv + (size_t)key * kDim + dma_chunk * 16,
+                                         (__attribute__((address_space(3))) void*)(skv + blk * 1024), 16, 0, 0);
+      }
+      for (int i = wave; i < kTileKeys / 64; i += WAVES) {
+        const int key = min(tile + 64 * i + lane, n - 1);
+        __builtin_amdgcn_global_load_lds(a.kv_scale + key, (__attribute__((address_space(3))) void*)(ssc + 64 * i),
+                                         4, 0, 0);
       }
     };
-    // LDS offsets of this thread's chunks in a tile buffer (rows swizzled by key & 7), fixed per thread
-    int soff[kChunksPerThread];
-#pragma unroll
-    for (int c2 = 0; c2 < kChunksPerThread; ++c2) {
-      const int ci = tid + c2 * kThreads;
-      const int key = ci >> 3;
-      soff[c2] = key * kDim + (((ci & 7) ^ (key & 7)) * 16);
-    }
-    auto lstore = [&](int buf) {
-      uint8_t* sb = &s_kv[buf][0];
-#pragma unroll
-      for (int c2 = 0; c2 < kChunksPerThread; ++c2) *reinterpret_cast<v4i*>(sb + soff[c2]) = stage[c2];
-      if (tid < kTileKeys) s_scale[buf][tid] = stage_scale;
-    };
 
-    gload(tile_lo);
-    for (int it = 0; it < ntiles; ++it) {
-      const int buf = it & 1;
-      const int tile = tile_lo + it * kTileKeys;
-      lstore(buf);
-      __syncthreads();
-      if (it + 1 < ntiles) gload(tile + kTileKeys);
-      const uint8_t* tbase = &s_kv[buf][0];
-      if (tile >= w_lo && tile + kTileKeys <= w_hi) {
+    // A tile's logits are stored after the next tile's barrier, so that the wait for each tile's
+    // loads before that barrier never waits on freshly issued stores.
+    float pv[kFrags];
+    int p_tile = -1;
+    bool p_interior = false;
+    auto store_tile = [&]() {
+      const int tile = p_tile;
+      if (p_interior) {
         // interior tile: every key is inside every row's window
         float* __restrict__ optr = out_row + tile + kl;
 #pragma unroll
-        for (int f = 0; f < kTileKeys / 16; ++f) {
-          const v4i b0 = *reinterpret_cast<const v4i*>(tbase + f * 16 * kDim + boff0);
-          const v4i b1 = *reinterpret_cast<const v4i*>(tbase + f * 16 * kDim + boff1);
-          const v8i b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-          optr[f * 16] = fragment_logit(qf, b) * s_scale[buf][f * 16 + kl];
-        }
+        for (int f = 0; f < kFrags; ++f) optr[f * 16] = pv[f];
       } else {
 #pragma unroll
-        for (int f = 0; f < kTileKeys / 16; ++f) {
-          const int key = f * 16 + kl;
-          const v4i b0 = *reinterpret_cast<const v4i*>(tbase + f * 16 * kDim + boff0);
-          const v4i b1 = *reinterpret_cast<const v4i*>(tbase + f * 16 * kDim + boff1);
-          const v8i b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-          const float v = fragment_logit(qf, b) * s_scale[buf][key];
-          const int j = tile + key;
+        for (int f = 0; f < kFrags; ++f) {
+          const int j = tile + f * 16 + kl;
           if (row_ok && j < tile_end) {
             if (j >= my_ks && j < my_ke) {
-              out_row[j] = v;
+              out_row[j] = pv[f];
             } else if (clean) {
               out_row[j] = -INFINITY;
             }
           }
         }
       }
+    };
+    auto tile_step = [&](int it, const uint8_t* cur_kv, const float* cur_sc, uint8_t* nxt_kv, float* nxt_sc) {
+      const int tile = tile_lo + it * kTileKeys;
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the tile have landed (and its older stores)
+      __syncthreads();                 // ... and every wave's: the tile is in LDS, the other buffer is free
+      if (it + 1 < ntiles) dma(tile + kTileKeys, nxt_kv, nxt_sc);
+      if (p_tile >= 0) store_tile();
+#pragma unroll
+      for (int f = 0; f < kFrags; ++f) {
+        const v4i b0 = *reinterpret_cast<const v4i*>(cur_kv + f * 16 * kDim + boff0);
+        const v4i b1 = *reinterpret_cast<const v4i*>(cur_kv + f * 16 * kDim + boff1);
+        const v8i b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        pv[f] = fragment_logit(qf, b) * cur_sc[f * 16 + kl];
+      }
+      p_tile = tile;
+      p_interior = tile >= w_lo && tile + kTileKeys <= w_hi;
+    };
+
+    dma(tile_lo, s_kv0, s_sc0);
+    for (int it = 0; it < ntiles; it += 2) {
+      tile_step(it, s_kv0, s_sc0, s_kv1, s_sc1);
+      if (it + 1 < ntiles) tile_step(it + 1, s_kv1, s_sc1, s_kv0, s_sc0);
     }
+    store_tile();
   }
 }
 
