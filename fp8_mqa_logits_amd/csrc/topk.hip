@@ -8,7 +8,7 @@
 // Keys are compared as order-preserving uint32 codes of the floats (-0.0 is
 // folded onto +0.0; code 0 marks padding).
 //
-// Algorithm: one workgroup of 256 threads per (row, segment of at most 65536
+// Algorithm: one workgroup of 256 threads per (row, segment of at most 70016
 // keys), streaming the segment from memory; nothing is held per key in
 // registers, so several workgroups share a CU and their loads overlap each
 // other's selection work.
@@ -82,7 +82,8 @@ struct TopkKernelArgs {
 
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
-constexpr int64_t kMaxSeg = 65536;                                // keys per segment
+// Keys per segment: the largest whose bitmaps keep the workgroup's LDS at three per CU (52 KB).
+constexpr int64_t kMaxSeg = 70016;
 // Position bitmap words of a segment of up to `seg` keys (positions count from the 16-byte load base).
 constexpr int bitmap_words(int64_t seg) { return (int)((seg + 4 + 31) / 32) + 1; }
 constexpr int kBitmapWords = bitmap_words(kMaxSeg);

@@ -172,7 +172,7 @@ def test_fused_workspace_covers_chunk_and_candidates(lib):
     ws = F.fp8idx_workspace_bytes(F.OP_LOGITS_TOPK_RAGGED, 7500, 210000, 2048, cap)
     # the cap allows 2380 rows per chunk: 4 chunks, so 1875 rows each
     logits = 1875 * 210000 * 4
-    cand = 1875 * 4 * 2048 * 8          # 4 segments of up to 52500 keys per row
+    cand = 1875 * 3 * 2048 * 8          # 3 segments of 70000 keys per row
     assert ws >= logits + cand
     assert ws <= logits + cand + 4096
     # one-shot on 8192 x 65536: the work-queue counters and the full 2 GiB buffer, single-segment top-k
