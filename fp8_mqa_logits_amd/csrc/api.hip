@@ -715,6 +715,7 @@ fp8idx_status indexer_logits_topk_paged(const uint8_t* q, const uint8_t* kv_pool
 
 size_t fp8idx_workspace_bytes_paged(int32_t B, int32_t next_n, int32_t width, int32_t k, size_t logits_cap_bytes) {
   if (B <= 0 || next_n <= 0 || width < 0 || k < 1 || k > fp8idx::kMaxK) return 0;
+  if ((int64_t)B * next_n > INT32_MAX) return 0;   // the entry rejects such a call
   return fused_layout(B * next_n, width, k, logits_cap_bytes, next_n, false).total;
 }
 

@@ -445,7 +445,9 @@ FP8IDX_API size_t fp8idx_sparse_mla_workspace_bytes(int32_t T, int32_t H, int32_
 FP8IDX_API size_t fp8idx_workspace_bytes(int32_t op, int32_t rows, int64_t width, int32_t k,
                               size_t logits_cap_bytes);
 
-/* Bytes of workspace indexer_logits_topk_paged needs.  Pure host arithmetic. */
+/* Bytes of workspace indexer_logits_topk_paged needs.  Pure host arithmetic.
+ * Returns 0 for arguments the entry rejects (B or next_n < 1, width < 0, k
+ * outside [1, 16384], B * next_n past INT32_MAX). */
 FP8IDX_API size_t fp8idx_workspace_bytes_paged(int32_t B, int32_t next_n, int32_t width, int32_t k,
                                     size_t logits_cap_bytes);
 

@@ -153,6 +153,9 @@ def test_fused_validation(lib):
     assert g(*pargs) == EWS
     pargs[20] = lib.fp8idx_workspace_bytes_paged(2, 4, 256, 64, 0)
     assert g(*pargs) == EDEV
+    # the size query answers 0 where the entry rejects the rows (B * next_n past int32)
+    assert lib.fp8idx_workspace_bytes_paged(1 << 20, 1 << 12, 256, 64, 0) == 0
+    assert lib.fp8idx_workspace_bytes_paged(2, 0, 256, 64, 0) == 0
 
 
 def test_rows_per_chunk_follows_chunking_page(lib):
