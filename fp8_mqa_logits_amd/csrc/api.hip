@@ -150,13 +150,16 @@ fp8idx_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
 }
 
 // Layout of the fused entries' workspace: [queue counters (ragged only)] [chunk logits x buffers]
-// [top-k candidates].  ok is false when the arguments are rejected (an unsupported top-k plan).
+// [fragment maxima (paged, when the top-k takes them)] [top-k candidates].  ok is false when the
+// arguments are rejected (an unsupported top-k plan).
 struct FusedLayout {
   bool ok;
   int32_t rpc;          // rows per chunk
   size_t queue_bytes;   // work-queue counters of the ragged logits launches
   size_t buf_bytes;     // one chunk of logits
   int32_t buffers;      // chunk logits buffers (2 when the overlap entry alternates them)
+  int64_t ld_frag;      // fragment maxima per row (16-key fragments of the width)
+  size_t frag_bytes;    // one chunk's fragment maxima (paged, one-workgroup-per-row top-k), else 0
   size_t topk_bytes;    // candidates of the largest chunk's top-k
   size_t total;
 };
@@ -184,8 +187,11 @@ FusedLayout fused_layout(int32_t rows, int64_t width, int32_t k, size_t cap, int
   L.queue_bytes = ragged ? fp8idx::kRaggedQueueBytes : 0;
   L.buf_bytes = align256((size_t)rpc * (size_t)ld * 4u);
   L.buffers = rpc < rows ? logit_buffers : 1;
+  L.ld_frag = (width + 15) / 16;
+  const bool frag = !ragged && (fp8idx::topk_plan_takes_frag_max(p0) || fp8idx::topk_plan_takes_frag_max(p1));
+  L.frag_bytes = frag ? align256((size_t)rpc * (size_t)L.ld_frag * 4u) : 0;
   L.topk_bytes = std::max(fp8idx::topk_workspace_bytes(p0), fp8idx::topk_workspace_bytes(p1));
-  L.total = L.queue_bytes + L.buf_bytes * (size_t)L.buffers + L.topk_bytes;
+  L.total = L.queue_bytes + L.buf_bytes * (size_t)L.buffers + L.frag_bytes + L.topk_bytes;
   return L;
 }
 
@@ -682,7 +688,8 @@ fp8idx_status indexer_logits_topk_paged(const uint8_t* q, const uint8_t* kv_pool
   const int32_t rpc = L.rpc;
   const int32_t req_per_chunk = std::max<int32_t>(1, rpc / next_n);
   float* chunk_logits = static_cast<float*>(ws);
-  void* topk_ws = static_cast<uint8_t*>(ws) + L.buf_bytes;
+  uint32_t* frag_max = L.frag_bytes ? reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + L.buf_bytes) : nullptr;
+  void* topk_ws = static_cast<uint8_t*>(ws) + L.buf_bytes + L.frag_bytes;
   fp8idx::TopkMap kmap{};
   if (map_to_slots) {
     kmap.kind = FP8IDX_MAP_BLOCK_TABLE;
@@ -699,14 +706,17 @@ fp8idx_status indexer_logits_topk_paged(const uint8_t* q, const uint8_t* kv_pool
     const int32_t nb = std::min(req_per_chunk, B - b0);
     const int32_t r0 = b0 * next_n;
     const int32_t nr = nb * next_n;
+    // the top-k of a chunk whose rows each take one workgroup starts from the logits kernel's
+    // per-fragment maxima
+    const fp8idx::TopkPlan plan = fp8idx::plan_topk(nr, width, k);
+    uint32_t* fm = fp8idx::topk_plan_takes_frag_max(plan) ? frag_max : nullptr;
     fp8idx::PagedLogitsArgs la{q + (size_t)r0 * fp8idx::kQRowBytesHost, kv_pool, scale_pool,
                                weights + (size_t)r0 * 32, row_len + r0, block_table + (int64_t)b0 * max_pages,
-                               nb, next_n, max_pages, num_pages, chunk_logits, ld, width, 0};
+                               nb, next_n, max_pages, num_pages, chunk_logits, ld, width, 0, fm, L.ld_frag};
     hipError_t e = fp8idx::launch_logits_paged(la, dev, st);
     if (e != hipSuccess) return hip_fail(e);
-    const fp8idx::TopkPlan plan = fp8idx::plan_topk(nr, width, k);
     fp8idx::TopkArgs ta{chunk_logits, ld, nr, width, nullptr, row_len + r0, k, r0, kmap,
-                        out + (int64_t)r0 * ld_out, ld_out};
+                        out + (int64_t)r0 * ld_out, ld_out, fm, L.ld_frag};
     e = fp8idx::launch_topk(ta, plan, topk_ws, st);
     if (e != hipSuccess) return hip_fail(e);
   }

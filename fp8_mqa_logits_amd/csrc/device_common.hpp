@@ -53,6 +53,16 @@ __device__ __forceinline__ uint32_t float_to_ordered(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Largest value over each 16-lane row of the wave, in every lane of the row (DPP: quad swaps, then
+// the half-row and row mirrors).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0, (int)x, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0, (int)x, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0, (int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0, (int)x, 0x140, 0xF, 0xF, false));  // row_mirror
+  return x;
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Number of set bits of a 64-bit wave mask below this lane.

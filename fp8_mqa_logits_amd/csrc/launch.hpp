@@ -44,6 +44,11 @@ struct PagedLogitsArgs {
   int64_t ld;
   int32_t width;
   int32_t clean;
+  // Optional (null: not written): per (row, 16-key fragment f) the largest order code
+  // (float_to_ordered) of the row's logits at keys [16 f, 16 f + 16) inside its window, at
+  // frag_max[row * ld_frag + f], for every fragment that holds a key of the row's window.
+  uint32_t* frag_max;
+  int64_t ld_frag;
 };
 
 struct TopkMap {
@@ -69,6 +74,10 @@ struct TopkArgs {
   TopkMap map;
   int32_t* out;
   int64_t ld_out;
+  // Optional: the fragment maxima the paged logits kernel wrote for these logits (see
+  // PagedLogitsArgs::frag_max); used by the one-workgroup-per-row configuration when ks is null.
+  const uint32_t* frag_max;
+  int64_t ld_frag;
 };
 
 // Host-side plan of the multi-level top-k: level 0 splits each row into
@@ -105,6 +114,8 @@ void query_paged_occupancy(DeviceInfo& d);
 
 TopkPlan plan_topk(int32_t rows, int64_t width, int32_t k);
 size_t topk_workspace_bytes(const TopkPlan& p);
+// True when launch_topk under this plan takes fragment maxima (one workgroup per whole row).
+bool topk_plan_takes_frag_max(const TopkPlan& p);
 
 hipError_t launch_logits_ragged(const RaggedLogitsArgs& a, const DeviceInfo& dev, hipStream_t s);
 // Device address of the current device's static work-queue counters (logits_ragged.hip), looked up

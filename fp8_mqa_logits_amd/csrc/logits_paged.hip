@@ -28,6 +28,10 @@
 // - With clean set, keys past a unit's scored range are filled with -inf by a
 //   second balanced split over (unit, 64-key block) pairs.  Keys inside a
 //   row's window whose page id lies outside the pool get -inf in any case.
+// - On request, each row's largest logit code per 16-key fragment is written
+//   too (a 16-lane DPP max of the stored values): the top-k that follows in
+//   the fused entry takes its threshold from these maxima and reads only the
+//   fragments that reach it.
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -227,11 +231,23 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
 #pragma unroll
       for (int f = 0; f < kFragsPerPage; ++f)
         v[f] = fragment_logit(qf, pf.b[f]) * __shfl(pf.sc, f * 16 + (lane & 15));
+      uint32_t fmax[kFragsPerPage];
 #pragma unroll
       for (int f = 0; f < kFragsPerPage; ++f) {
         const int j = (cur_pg + i) * kPage + f * 16 + (lane & 15);
         const bool inwin = j < my_len;
-        if (live && row_ok && j < covered && (inwin || clean)) out_row[j] = ok && inwin ? v[f] : -INFINITY;
+        const float st = ok && inwin ? v[f] : -INFINITY;
+        if (live && row_ok && j < covered && (inwin || clean)) out_row[j] = st;
+        // the fragment's largest in-window code for the top-k (0 for keys outside the window)
+        if (a.frag_max) fmax[f] = row16_max_u32(live && row_ok && inwin ? float_to_ordered(st) : 0u);
+      }
+      if (a.frag_max) {
+        // lanes 0..3 of each 16-lane row store that row's four fragment maxima of this page
+        const int c = lane & 15;
+        const int64_t fidx = (int64_t)(cur_pg + i) * kFragsPerPage + c;
+        const uint32_t m = c == 0 ? fmax[0] : c == 1 ? fmax[1] : c == 2 ? fmax[2] : fmax[3];
+        if (live && row_ok && c < kFragsPerPage && fidx < a.ld_frag && fidx * 16 < covered)
+          a.frag_max[(int64_t)(t.r_base + my_q) * a.ld_frag + fidx] = m;
       }
     };
     // One page loads while the previous one is scored; the chunk's last step

@@ -38,9 +38,17 @@
 // same exact selection and ordering run over every key of the segment,
 // streamed from memory once per step.
 // Few long rows (at most 512 rows of at most 131072 keys, k up to about
-// 2800: paged decode) take one 512-thread workgroup per whole row instead:
+// 2300: paged decode) take one 512-thread workgroup per whole row instead:
 // twice the loads in flight of a 256-thread segment, a single launch and no
 // merge level (position bitmaps sized for 131072 keys, one workgroup per CU).
+// In the fused paged entry the logits kernel also hands over each row's
+// largest key code per 16-key fragment.  The kk-th largest fragment maximum T
+// is at most the kk-th largest key (at least kk fragments, hence kk keys,
+// reach it), and every key >= T sits in a fragment whose maximum reaches T:
+// so a row of at least 1.5 kk fragments lists the fragments >= T, reads only
+// those (four lanes per 64-byte fragment), and keeps their keys >= T.  On the
+// decode rows that is about a quarter of the fragments and 1.15-1.75 kk
+// candidates; a list that would overflow falls back to the sampled path.
 // Other rows longer than one segment, or few rows that need more parallelism, are
 // split: each segment emits its local top-k (code, index) pairs in index
 // order, and further levels of the same kernel select from the concatenated
@@ -78,6 +86,8 @@ struct TopkKernelArgs {
   int32_t* out_idx;
   int32_t row0;
   TopkMap map;
+  const uint32_t* frag_max;   // per (row, 16-key fragment) largest key code, or null
+  int64_t ld_frag;
 };
 
 constexpr int kDigitBits = 11;
@@ -170,6 +180,7 @@ struct TopkShared {
   uint32_t w1[NW];
   uint32_t w2[NW];
   uint32_t cnt;
+  uint32_t nfrag_listed;            // fragments reaching the threshold (fragment-maximum path)
   uint32_t nb;
   uint32_t digit;
   uint32_t above;
@@ -441,8 +452,10 @@ __device__ __forceinline__ void append_candidates(const uint32_t (&c)[UNR][VEC],
       }
 }
 
-template <int THREADS, int CAP, int SEG, bool LEVEL0, bool FINAL, int VEC>
+template <int THREADS, int CAP, int SEG, bool LEVEL0, bool FINAL, int VEC, bool FM = false>
 __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
+  static_assert(!FM || (LEVEL0 && VEC == 4 && (SEG + 15) / 16 <= kSampleRuns * THREADS),
+                "fragment maxima: a window's fragments fit the per-thread sample registers");
   constexpr int NW = THREADS / 64;
   constexpr int UNR = kElemsPerPass / VEC;   // vectors per thread per pass
   static_assert(kBins % THREADS == 0, "bins per thread");
@@ -455,6 +468,17 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
   const int lane = tid & 63;
   const int row = blockIdx.x / a.nseg;
   const int seg = blockIdx.x - row * a.nseg;
+  // The row's fragment maxima (fragment b * THREADS + tid) load first, beside the window bounds.
+  uint32_t fc[FM ? kSampleRuns : 1];
+  if constexpr (FM) {
+    if (a.frag_max != nullptr) {
+#pragma unroll
+      for (int b = 0; b < kSampleRuns; ++b) {
+        const int f = b * THREADS + tid;
+        fc[b] = f < a.ld_frag ? a.frag_max[(int64_t)row * a.ld_frag + f] : 0u;
+      }
+    }
+  }
 
   // ---- segment window --------------------------------------------------------
   int row_ks = 0;
@@ -522,6 +546,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
   if (tid == 0) {
     sh.cnt = 0u;
     sh.nb = 0u;
+    sh.nfrag_listed = 0u;
   }
 
   // Streaming passes of the compaction below: pass 0 is loaded as soon as the
@@ -540,87 +565,210 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
   bool try_list = true;     // false: the list cannot hold the candidates
   uint32_t bshift = 0u;     // candidate bins: min((code - T) >> bshift, kBins - 1)
   uint32_t kk = (uint32_t)min(a.k, len);   // level 0: every position of the window is a key
-  if (len > CAP) {
-    uint32_t sc[kSampleRuns];
+  // Fragment maxima (when the logits kernel wrote them): fragment f holds keys [16 f, 16 f + 16) of a
+  // window that starts at key 0.  At least kk fragments have a maximum >= the kk-th largest
+  // fragment maximum, so at least kk keys do: that value bounds the kk-th largest key from below,
+  // and every key at or above it lies in a fragment whose maximum reaches it.  With at least 1.5 kk
+  // fragments the bound sits high enough that the keys reaching it fit the list (1.15 to 1.75 kk on
+  // the decode rows); if they do not (ties, values crowding into few fragments), the sampled
+  // threshold and the streamed compaction below run instead.
+  const int nfrag = (len + 15) / 16;
+  uint32_t C = 0xffffffffu;
+  bool listed = false;   // the candidate list came from the fragment maxima
+  auto cand_bin = [&](uint32_t code) { return min((code - T) >> bshift, (uint32_t)(kBins - 1)); };
+  if (FM && a.frag_max != nullptr && len > CAP && 2 * nfrag >= 3 * (int)kk && sa == 0) {
+#pragma unroll
+    for (int b = 0; b < kSampleRuns; ++b) fc[b] = b * THREADS + tid < nfrag ? max(fc[b], 1u) : 0u;   // 0: none
+    uint32_t fmin = 0xffffffffu, fmax = 0u, nf = 0u;
 #pragma unroll
     for (int b = 0; b < kSampleRuns; ++b) {
-      const int start = src.off + (int)((int64_t)b * (len - THREADS) / (kSampleRuns - 1));
-      sc[b] = src.code_at(start + tid);
-    }
-    if (nvec > 0) {
-      load_pass(0, c);
-      c_loaded = true;
-      __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of the threshold work
-    }
-    uint32_t smin = 0xffffffffu, smax = 0u, ns = 0u;
-#pragma unroll
-    for (int b = 0; b < kSampleRuns; ++b) {
-      if (sc[b] != 0u) {
-        smin = min(smin, sc[b]);
-        smax = max(smax, sc[b]);
-        ++ns;
+      if (fc[b] != 0u) {
+        fmin = min(fmin, fc[b]);
+        fmax = max(fmax, fc[b]);
+        ++nf;
       }
     }
-    block_min_max_sum<NW>(smin, smax, ns, sh.w0, sh.w1, sh.w2);
-    // sample rank whose code should leave ~1.3 k keys at or above it
-    const uint64_t want = ((uint64_t)kk * kSampleSize * 13u + 10ull * len - 1u) / (10ull * len) + 16u;
-    if (ns > 0u && want < ns && want * (uint64_t)len <= (uint64_t)CAP * kSampleSize * 7u / 8u) {
-      uint32_t unused;
-      T = radix_select<THREADS>(
-          [&](auto&& visit) {
+    block_min_max_sum<NW>(fmin, fmax, nf, sh.w0, sh.w1, sh.w2);
+    uint32_t unused;
+    // slack 16: T is the lowest code of a bin holding the kk-th largest maximum, so at least kk
+    // (and fewer than kk + 16, bar ties) fragments reach it
+    uint32_t Tf = radix_select<THREADS>(
+        [&](auto&& visit) {
 #pragma unroll
-            for (int b = 0; b < kSampleRuns; ++b)
-              if (sc[b] != 0u) visit(sc[b]);
-          },
-          smin, smax, (uint32_t)want, 16u, unused, sh);
-      T = max(T, 1u);
-      sampled = true;
-      const uint32_t range = smax - min(T, smax);
-      bshift = range >> kDigitBits ? (uint32_t)(32 - __builtin_clz(range) - kDigitBits) : 0u;
-    } else if (LEVEL0) {
-      try_list = false;   // every key would be a candidate, more than the list holds
+          for (int b = 0; b < kSampleRuns; ++b)
+            if (fc[b] != 0u) visit(fc[b]);
+        },
+        fmin, fmax, kk, 16u, unused, sh);
+    Tf = max(Tf, 1u);
+    // The fragments whose maximum reaches Tf, listed in LDS (the histogram array is free until the
+    // selection), then read 16 keys at a time; their keys >= Tf form the candidate list.
+    uint32_t* flist = sh.hist;
+    constexpr int kFragListCap = WORDS;
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int b = 0; b < kSampleRuns; ++b) mine += fc[b] >= Tf ? 1u : 0u;
+    uint32_t incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t t = (uint32_t)__shfl_up((int)incl, o);
+      if (lane >= o) incl += t;
     }
-  }
-  if (sampled) {
+    uint32_t fbase = 0u;
+    if (lane == 63 && incl > 0u) fbase = atomicAdd(&sh.nfrag_listed, incl);
+    fbase = __builtin_amdgcn_readlane(fbase, 63);
+    uint32_t fslot = fbase + incl - mine;
 #pragma unroll
-    for (int i = 0; i < kBins / THREADS; ++i) sh.hist[tid * (kBins / THREADS) + i] = 0u;
-  }
-  __syncthreads();
-  auto cand_bin = [&](uint32_t code) { return min((code - T) >> bshift, (uint32_t)(kBins - 1)); };
-
-  // ---- 2. compaction of the codes >= T ----------------------------------------
-  uint32_t C = 0xffffffffu;
-  if (try_list) {
-    // Every lane runs every pass (the slot scan below is wave-wide); the next
-    // pass's loads are in flight while this pass's keys are appended.  Keys are
-    // loaded raw.  With the threshold above +0.0, a level-0 key is a candidate
-    // exactly when its bits, read as a signed int, reach T - 2^31: negative
-    // floats, -0.0 and negative NaNs are negative ints, and the code of a
-    // non-negative float is its bits with the sign bit set.  A pass whose
-    // vectors all lie in the window then costs one compare per key; other
-    // passes take the general test on codes.
-    const bool raw_cmp = LEVEL0 && T > 0x80000000u;
-    const int Ti = (int)(T - 0x80000000u);
-    if (nvec > 0 && !c_loaded) load_pass(0, c);
-    for (int vb = 0; vb < nvec; vb += kPass) {
-      uint32_t nx[UNR][VEC];
-      const bool more = vb + kPass < nvec;
-      if (more) load_pass(vb + kPass, nx);
-      const int v0 = vb + tid;
-      if (raw_cmp && vb * VEC >= src.off && (vb + kPass) * VEC <= src.span)
-        append_candidates<true, THREADS, CAP, UNR, VEC>(c, v0, nvec, src, T, Ti, lane, sh);
-      else
-        append_candidates<false, THREADS, CAP, UNR, VEC>(c, v0, nvec, src, T, Ti, lane, sh);
-      if (more) {
+    for (int b = 0; b < kSampleRuns; ++b)
+      if (fc[b] >= Tf) {
+        if (fslot < (uint32_t)kFragListCap) flist[fslot] = (uint32_t)(b * THREADS + tid);
+        ++fslot;
+      }
+    __syncthreads();
+    const uint32_t nq = sh.nfrag_listed;
+    if (nq <= (uint32_t)kFragListCap) {
+      // Four consecutive lanes read one fragment (16 bytes each), so a load instruction covers 16
+      // fragments; kQ loads per thread cover THREADS * kQ / 4 listed fragments per round trip.
+      constexpr int kQ = 18;
+      const float* rowp = src.f;   // window start (key 0) at a 16-byte boundary
+      const int64_t last4 = a.ld - 4;   // last 16-byte load inside the row
+      const int quarter = tid & 3;
+      for (uint32_t q0 = 0; q0 < nq; q0 += THREADS * kQ / 4) {
+        v4f d[kQ];
+        int key0[kQ];   // position of d[j][0]
 #pragma unroll
-        for (int u = 0; u < UNR; ++u)
+        for (int j = 0; j < kQ; ++j) {
+          const uint32_t qi = q0 + (uint32_t)(j * (THREADS / 4) + (tid >> 2));
+          key0[j] = (int)flist[min(qi, nq - 1u)] * 16 + 4 * quarter;
+          d[j] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(rowp + min((int64_t)key0[j], last4)));
+        }
+        auto take = [&](int j, int e) -> bool {
+          return q0 + (uint32_t)(j * (THREADS / 4) + (tid >> 2)) < nq && key0[j] + e < len &&
+                 SegmentSource<LEVEL0, VEC>::float_code(d[j][e]) >= Tf;
+        };
+        uint32_t cm = 0u;
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) c[u][i] = nx[u][i];
+        for (int j = 0; j < kQ; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cm += take(j, e) ? 1u : 0u;
+        uint32_t ci = cm;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t t = (uint32_t)__shfl_up((int)ci, o);
+          if (lane >= o) ci += t;
+        }
+        uint32_t cbase = 0u;
+        if (lane == 63 && ci > 0u) cbase = atomicAdd(&sh.cnt, ci);
+        cbase = __builtin_amdgcn_readlane(cbase, 63);
+        uint32_t cslot = cbase + ci - cm;
+#pragma unroll
+        for (int j = 0; j < kQ; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (take(j, e)) {
+              sh.cand[min(cslot, (uint32_t)CAP)] =
+                  v2u{SegmentSource<LEVEL0, VEC>::float_code(d[j][e]), (uint32_t)(key0[j] + e)};
+              ++cslot;
+            }
       }
     }
     __syncthreads();
-    C = sh.cnt;
-    if (!LEVEL0 && !sampled) kk = min((uint32_t)a.k, C);   // C counted every key
+    const uint32_t cf = sh.nfrag_listed <= (uint32_t)WORDS ? sh.cnt : 0xffffffffu;
+    __syncthreads();   // every thread has read the counts
+    if (cf >= kk && cf <= (uint32_t)CAP) {
+      listed = true;
+      C = cf;
+      T = Tf;
+      sampled = true;
+      const uint32_t range = fmax - min(T, fmax);
+      bshift = range >> kDigitBits ? (uint32_t)(32 - __builtin_clz(range) - kDigitBits) : 0u;
+#pragma unroll
+      for (int i = 0; i < kBins / THREADS; ++i) sh.hist[tid * (kBins / THREADS) + i] = 0u;
+    } else if (tid == 0) {
+      sh.cnt = 0u;
+    }
+    __syncthreads();
+  }
+  if (!listed) {
+    if (len > CAP) {
+      uint32_t sc[kSampleRuns];
+#pragma unroll
+      for (int b = 0; b < kSampleRuns; ++b) {
+        const int start = src.off + (int)((int64_t)b * (len - THREADS) / (kSampleRuns - 1));
+        sc[b] = src.code_at(start + tid);
+      }
+      if (nvec > 0) {
+        load_pass(0, c);
+        c_loaded = true;
+        __builtin_amdgcn_sched_barrier(0);   // keep these loads ahead of the threshold work
+      }
+      uint32_t smin = 0xffffffffu, smax = 0u, ns = 0u;
+#pragma unroll
+      for (int b = 0; b < kSampleRuns; ++b) {
+        if (sc[b] != 0u) {
+          smin = min(smin, sc[b]);
+          smax = max(smax, sc[b]);
+          ++ns;
+        }
+      }
+      block_min_max_sum<NW>(smin, smax, ns, sh.w0, sh.w1, sh.w2);
+      // sample rank whose code should leave ~1.3 k keys at or above it
+      const uint64_t want = ((uint64_t)kk * kSampleSize * 13u + 10ull * len - 1u) / (10ull * len) + 16u;
+      if (ns > 0u && want < ns && want * (uint64_t)len <= (uint64_t)CAP * kSampleSize * 7u / 8u) {
+        uint32_t unused;
+        T = radix_select<THREADS>(
+            [&](auto&& visit) {
+#pragma unroll
+              for (int b = 0; b < kSampleRuns; ++b)
+                if (sc[b] != 0u) visit(sc[b]);
+            },
+            smin, smax, (uint32_t)want, 16u, unused, sh);
+        T = max(T, 1u);
+        sampled = true;
+        const uint32_t range = smax - min(T, smax);
+        bshift = range >> kDigitBits ? (uint32_t)(32 - __builtin_clz(range) - kDigitBits) : 0u;
+      } else if (LEVEL0) {
+        try_list = false;   // every key would be a candidate, more than the list holds
+      }
+    }
+    if (sampled) {
+#pragma unroll
+      for (int i = 0; i < kBins / THREADS; ++i) sh.hist[tid * (kBins / THREADS) + i] = 0u;
+    }
+    __syncthreads();
+
+    // ---- 2. compaction of the codes >= T ----------------------------------------
+    if (try_list) {
+      // Every lane runs every pass (the slot scan below is wave-wide); the next
+      // pass's loads are in flight while this pass's keys are appended.  Keys are
+      // loaded raw.  With the threshold above +0.0, a level-0 key is a candidate
+      // exactly when its bits, read as a signed int, reach T - 2^31: negative
+      // floats, -0.0 and negative NaNs are negative ints, and the code of a
+      // non-negative float is its bits with the sign bit set.  A pass whose
+      // vectors all lie in the window then costs one compare per key; other
+      // passes take the general test on codes.
+      const bool raw_cmp = LEVEL0 && T > 0x80000000u;
+      const int Ti = (int)(T - 0x80000000u);
+      if (nvec > 0 && !c_loaded) load_pass(0, c);
+      for (int vb = 0; vb < nvec; vb += kPass) {
+        uint32_t nx[UNR][VEC];
+        const bool more = vb + kPass < nvec;
+        if (more) load_pass(vb + kPass, nx);
+        const int v0 = vb + tid;
+        if (raw_cmp && vb * VEC >= src.off && (vb + kPass) * VEC <= src.span)
+          append_candidates<true, THREADS, CAP, UNR, VEC>(c, v0, nvec, src, T, Ti, lane, sh);
+        else
+          append_candidates<false, THREADS, CAP, UNR, VEC>(c, v0, nvec, src, T, Ti, lane, sh);
+        if (more) {
+#pragma unroll
+          for (int u = 0; u < UNR; ++u)
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) c[u][i] = nx[u][i];
+        }
+      }
+      __syncthreads();
+      C = sh.cnt;
+      if (!LEVEL0 && !sampled) kk = min((uint32_t)a.k, C);   // C counted every key
+    }
   }
 
   bool done = false;
@@ -915,6 +1063,8 @@ TopkPlan plan_topk(int32_t rows, int64_t width, int32_t k) {
 
 static size_t align256(size_t x) { return (x + 255u) & ~(size_t)255u; }
 
+bool topk_plan_takes_frag_max(const TopkPlan& p) { return p.supported && p.nlevels == 1 && p.level[0].cfg == 2; }
+
 size_t topk_workspace_bytes(const TopkPlan& p) {
   size_t total = 0;
   for (int b = 0; b < 2; ++b)
@@ -928,6 +1078,11 @@ static void launch_vec(bool vec4, unsigned grid, const TopkKernelArgs& a, hipStr
     hipLaunchKernelGGL((topk_kernel<THREADS, CAP, SEG, LEVEL0, FINAL, 4>), dim3(grid), dim3(THREADS), 0, s, a);
   else
     hipLaunchKernelGGL((topk_kernel<THREADS, CAP, SEG, LEVEL0, FINAL, 1>), dim3(grid), dim3(THREADS), 0, s, a);
+}
+
+static void launch_wide_frag_max(unsigned grid, const TopkKernelArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((topk_kernel<kWideThreads, kSmallCap, (int)kWideSeg, true, true, 4, true>), dim3(grid),
+                     dim3(kWideThreads), 0, s, a);
 }
 
 template <int CAP>
@@ -992,9 +1147,17 @@ hipError_t launch_topk(const TopkArgs& ta, const TopkPlan& plan, void* ws, hipSt
     }
     const int64_t grid = (int64_t)ta.rows * L.nseg;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (L.cfg == 2) launch_vec<kWideThreads, kSmallCap, (int)kWideSeg, true, true>(vec4, (unsigned)grid, a, s);
-    else if (L.cfg == 1) launch_cap<kBigCap>(level0, final_level, vec4, (unsigned)grid, a, s);
-    else launch_cap<kSmallCap>(level0, final_level, vec4, (unsigned)grid, a, s);
+    if (L.cfg == 2 && ta.frag_max != nullptr && vec4 && ta.ks == nullptr) {
+      a.frag_max = ta.frag_max;
+      a.ld_frag = ta.ld_frag;
+      launch_wide_frag_max((unsigned)grid, a, s);
+    } else if (L.cfg == 2) {
+      launch_vec<kWideThreads, kSmallCap, (int)kWideSeg, true, true>(vec4, (unsigned)grid, a, s);
+    } else if (L.cfg == 1) {
+      launch_cap<kBigCap>(level0, final_level, vec4, (unsigned)grid, a, s);
+    } else {
+      launch_cap<kSmallCap>(level0, final_level, vec4, (unsigned)grid, a, s);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

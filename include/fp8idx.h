@@ -267,7 +267,13 @@ FP8IDX_API fp8idx_status indexer_logits_topk_ragged_overlap(const uint8_t* q, co
  * logits exist at once (0 = all rows at once), spread evenly over the chunks.
  *   ws_bytes >= fp8idx_workspace_bytes_paged(B, next_n, width, k, logits_cap_bytes)
  * Chunks hold whole requests: at least one request per chunk even when one
- * request's next_n rows exceed the cap.
+ * request's next_n rows exceed the cap.  When a chunk's top-k takes one
+ * workgroup per row (at most 512 rows of at most 131072 keys, k up to about
+ * 2300), the logits kernel also writes each row's largest logit per 16-key
+ * fragment into the workspace (ceil(width / 16) words per row), and the top-k
+ * takes its threshold from those maxima: the kk-th largest of them is at most
+ * the row's kk-th largest logit, and only fragments that reach it are read.
+ * The result is the same exact selection either way.
  */
 FP8IDX_API fp8idx_status indexer_logits_topk_paged(const uint8_t* q, const uint8_t* kv_pool,
                                         const float* scale_pool, const float* weights,

@@ -182,6 +182,16 @@ def test_fused_workspace_covers_chunk_and_candidates(lib):
     assert F.fp8idx_workspace_bytes(F.OP_LOGITS_TOPK_RAGGED, 8192, 65536, 2048, 0) == 256 + 8192 * 65536 * 4
 
 
+def test_fused_paged_workspace_holds_fragment_maxima(lib):
+    # decode: 256 rows of 131072 keys, one top-k workgroup per row -> the chunk's logits, then one word
+    # per row and 16-key fragment, and no top-k candidates
+    assert F.fp8idx_workspace_bytes_paged(64, 4, 131072, 2048, 0) == 256 * 131072 * 4 + 256 * 8192 * 4
+    # rows longer than one workgroup takes (segmented top-k): no fragment maxima, the top-k's own
+    # candidate buffers instead
+    ws = F.fp8idx_workspace_bytes_paged(4, 4, 200000, 2048, 0)
+    assert ws == 16 * 200000 * 4 + F.fp8idx_workspace_bytes(F.OP_TOPK, 16, 200000, 2048, 0)
+
+
 def test_quant_validation(lib):
     f = lib.indexer_quant_fp8
     assert f(P, 128, 4, 130, P, 132, P, None) == EUNSUP      # D % 4 != 0

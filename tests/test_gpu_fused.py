@@ -74,6 +74,48 @@ def test_fused_paged_small():
         assert np.array_equal(slots.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("mode", ["random", "rising_scale", "zero_weights", "bad_pages"])
+@pytest.mark.parametrize("k", [2048, 300])
+def test_fused_paged_fragment_maxima(mode, k):
+    """Long decode rows, where the fused paged top-k (one workgroup per row) takes its threshold from
+    the logits kernel's per-16-key fragment maxima and reads only the fragments that reach it.  Value
+    mixes: scales rising along each context (the top keys crowd into the last pages), zero weights
+    (every logit ties, so the exact whole-row path runs), and page ids outside the pool (-inf
+    fragments).  Rows from 9000 to 131072 keys (shorter ones take the sampled threshold), three
+    chunks through one workspace.  Checked against the exact selection on the device's own logits."""
+    ctx = np.array([131072, 100000, 65537, 40000, 32769, 20000, 9000, 131071, 70000, 50001, 33000, 120000])
+    inp = paged_inputs(len(ctx), 3, 0, 131072, k, seed=70 + k, ctx=ctx)
+    if mode == "rising_scale":
+        for b, c in enumerate(ctx):
+            for p in range((int(c) + 63) // 64):
+                t = p * 64 + np.arange(64)
+                inp.scale_pool[inp.block_table[b, p]] = (0.5 + t / float(c)).astype(np.float32)
+    elif mode == "zero_weights":
+        inp.weights[:] = 0.0
+    elif mode == "bad_pages":
+        rng = np.random.default_rng(5)
+        for b, c in enumerate(ctx):
+            n_pages = (int(c) + 63) // 64
+            bad = rng.choice(n_pages, size=max(1, n_pages // 10), replace=False)
+            inp.block_table[b, bad] = np.where(rng.random(bad.size) < 0.5, -1, inp.kv_pool.shape[0] + 7)
+    width = inp.max_pages * 64
+    args = [to_dev(a) for a in (inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len, inp.block_table)]
+    ld = (width + 3) // 4 * 4
+    cap = 12 * ld * 4                                  # 4 requests per chunk: three chunks
+    slots = F.indexer_logits_topk_paged(*args, k, width=width, logits_cap_bytes=cap)
+    raw = F.indexer_logits_topk_paged(*args, k, width=width, map_to_slots=False, logits_cap_bytes=cap)
+    logits = F.indexer_logits_paged(*args, width=width, clean=True)
+    torch.cuda.synchronize()
+    g = logits.cpu().numpy().astype(np.float64)
+    zeros = np.zeros(inp.rows, np.int64)
+    exact = topk_indices(g, zeros, inp.row_len, k)
+    assert_topk_exact(raw.cpu().numpy(), exact, what=f"fragment maxima {mode} k{k}")
+    want = map_block_table(exact, list(range(inp.rows)), inp.next_n, inp.block_table, 64, inp.kv_pool.shape[0])
+    got = slots.cpu().numpy()
+    for i in range(inp.rows):
+        assert set(got[i].tolist()) == set(want[i].tolist()), f"{mode} k{k} slots row {i}"
+
+
 def _sample_rows(m, chunk):
     rows = {0, 1, m // 2, m - 2, m - 1}
     if chunk and chunk < m:
