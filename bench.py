@@ -14,8 +14,9 @@ prints one JSON line.
 
 Two timed regions run back to back, each after its own warm-up and each
 bracketed by synchronisations:
-  1. K steps of the fused entry: `value`, `ms_per_step` and the per-step
-     event distribution;
+  1. K steps of the fused entry: `value` and `ms_per_step` (the calls alone
+     between two synchronisations), then K more steps each bracketed by HIP
+     events for the per-step distribution;
   2. K steps of the same launches made one call at a time (the logits entry
      into the same chunk buffer, then the top-k entry), with HIP events on the
      launch stream between them: the per-launch durations behind `roofline`
@@ -404,17 +405,27 @@ def core_probe(cus, per_cu_list, iters, reps):
 
 
 def _time_fused(step, steps, warmup, overlap=False, cold=False):
-    """(wall ms per step, per-step event pairs) over `steps` calls of the fused entry (or the
-    overlapped one), each step bracketed by HIP events on the calling stream."""
+    """(ms per step, per-step event pairs) over `steps` calls of the fused entry (or the overlapped
+    one).  The timed loop holds the calls alone, between two synchronisations: a timing event pair
+    recorded inside every step costs GPU time of its own (about 13 us per step, 7% of a decode step).
+    The per-step distribution comes from a second loop of `steps` calls, each bracketed by events.
+    With `cold`, a scratch fill between steps evicts the caches and the step times are those events."""
     import torch
     run = step.run_overlap if overlap else step.run_fused
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if cold else None
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
+    t = None
+    if not cold:
+        _roctx().resume()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run()
+        torch.cuda.synchronize()
+        t = time.perf_counter() - t0
+        _roctx().pause()
     evs = []
-    _roctx().resume()
-    t0 = time.perf_counter()
     for i in range(steps):
         if cold:
             scratch.fill_(i & 0xff)
@@ -424,8 +435,6 @@ def _time_fused(step, steps, warmup, overlap=False, cold=False):
         e[1].record()
         evs.append(e)
     torch.cuda.synchronize()
-    t = time.perf_counter() - t0
-    _roctx().pause()
     if cold:
         return sum(a.elapsed_time(b) for a, b in evs) / steps, evs
     return t * 1e3 / steps, evs
@@ -715,17 +724,27 @@ def copy_calibration():
 def _timed_dispatches(n, steps, warmup):
     """Positions of the timed dispatches among a kernel's n dispatches in one run of this script.
 
-    Each of the two timed regions runs `warmup` steps, then `steps` timed steps, of identical
-    launches, so a kernel launched c times per step has n = 2 * (warmup + steps) * c dispatches, in
-    the order [warm-up, timed] of the fused region, then [warm-up, timed] of the call-by-call one.
-    Returns None when n does not fit that pattern (a kernel outside the timed regions)."""
-    per = 2 * (warmup + steps)
-    if n == 0 or n % per:
+    The fused region runs `warmup` steps, `steps` timed steps and `steps` steps with per-step events;
+    the call-by-call region runs `warmup` steps, then `steps` timed steps.  A kernel launched c times
+    per step in both regions has n = (2 * warmup + 3 * steps) * c dispatches; one that only the fused
+    entry launches (the paged top-k that reads the logits kernel's fragment maxima) has
+    (warmup + 2 * steps) * c, and one only the call-by-call region launches (warmup + steps) * c.
+    The warm-up dispatches are dropped.  Returns None when n fits none of these (a kernel outside the
+    timed regions)."""
+    if n == 0:
         return None
-    c = n // per
-    first = list(range(warmup * c, (warmup + steps) * c))
-    second = list(range((2 * warmup + steps) * c, (2 * warmup + 2 * steps) * c))
-    return first + second
+    both, fused, split = 2 * warmup + 3 * steps, warmup + 2 * steps, warmup + steps
+    if n % both == 0:
+        c = n // both
+        return (list(range(warmup * c, (warmup + 2 * steps) * c)) +
+                list(range((2 * warmup + 2 * steps) * c, (2 * warmup + 3 * steps) * c)))
+    if n % fused == 0:
+        c = n // fused
+        return list(range(warmup * c, (warmup + 2 * steps) * c))
+    if n % split == 0:
+        c = n // split
+        return list(range(warmup * c, (warmup + steps) * c))
+    return None
 
 
 def trace_summary(path, steps, warmup):
