@@ -25,6 +25,9 @@
 //   boundaries.  Every kv byte is read once and is shared by the 4 query rows.
 // - Scoring, ReLU, head weighting and the cross-lane head reduction are the
 //   same register-resident core as the ragged kernel.
+// - A chunk's logits (4 rows x 4 pages) collect in the wave's LDS buffer and
+//   leave as one contiguous 1 KiB store per row (16 bytes per lane), when the
+//   rows are 16-byte aligned; otherwise each key is stored on its own.
 // - With clean set, keys past a unit's scored range are filled with -inf by a
 //   second balanced split over (unit, 64-key block) pairs.  Keys inside a
 //   row's window whose page id lies outside the pool get -inf in any case.
@@ -45,6 +48,7 @@ constexpr int kPagedDepth = 2;         // pages in flight per wave, the scored o
 constexpr int kChunk = 4;              // pages a wave claims at a time
 constexpr int kMinChunksPerWg = 2;     // small totals run on fewer workgroups
 constexpr int kFragsPerPage = kPage / 16;   // 16-key MFMA fragments per page
+constexpr int kStageLd = kChunk * kPage + 16;   // row stride of a wave's logits staging buffer (floats)
 
 // One page's four B-operands (lane l: key l % 16 of each 16-key fragment,
 // bytes 32 * (l / 16) .. +32) and its 64 kv scales (lane l: key l).  The loads are unconditional (an
@@ -102,9 +106,15 @@ __device__ __forceinline__ int unit_chunks_at(const PagedLogitsArgs& a, int qgro
 static_assert(kPagedDepth == 2, "the chunk loop keeps one page in flight ahead of the scored one");
 static_assert(kChunk % kPagedDepth == 0, "chunks start on the first page buffer");
 
-template <int DEPTH>
+// VEC_STORE: the logits rows are 16-byte aligned (ld a multiple of 4, base aligned), so a chunk's
+// logits go out as 16-byte stores, one contiguous 1 KiB per row (see below); otherwise as one
+// 4-byte store per key.
+template <int DEPTH, bool VEC_STORE>
 __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(PagedLogitsArgs a, int qgroups) {
   __shared__ int s_next;   // next chunk of this workgroup's range to hand out
+  // Per wave: one chunk's logits of the unit's 4 rows, rows kStageLd floats apart (16 floats of
+  // padding keep the four rows' writes on different banks).
+  __shared__ float s_stage[kPagedWaves][4 * kStageLd];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -189,6 +199,7 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
   int covered = 0, my_len = 0;
   bool row_ok = false;
   float* __restrict__ out_row = a.logits;
+  float* const stage = s_stage[wave];
 
   while (nx_n > 0) {
     // the claimed chunk becomes the current one; the cursor still sits on its unit
@@ -237,7 +248,10 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
         const int j = (cur_pg + i) * kPage + f * 16 + (lane & 15);
         const bool inwin = j < my_len;
         const float st = ok && inwin ? v[f] : -INFINITY;
-        if (live && row_ok && j < covered && (inwin || clean)) out_row[j] = st;
+        if constexpr (VEC_STORE)
+          stage[my_q * kStageLd + i * kPage + f * 16 + (lane & 15)] = st;
+        else if (live && row_ok && j < covered && (inwin || clean))
+          out_row[j] = st;
         // the fragment's largest in-window code for the top-k (0 for keys outside the window)
         if (a.frag_max) fmax[f] = row16_max_u32(live && row_ok && inwin ? float_to_ordered(st) : 0u);
       }
@@ -261,6 +275,40 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
         np = nx_n > 0 ? __builtin_amdgcn_readfirstlane(nx_ids) : -1;
       load_page(a, np, lane, buf[(d + 1) % DEPTH]);
       score_page(d, buf[d % DEPTH]);
+    }
+    if constexpr (VEC_STORE) {
+      // The chunk's logits leave the staging buffer as one contiguous 1 KiB store per row: lane l
+      // writes keys 4 l .. 4 l + 3 of the chunk.  LDS operations of one wave complete in order, so
+      // these reads see the chunk's writes and the next chunk's writes come after them; the wave
+      // barriers keep the compiler from moving them.  Staged values already hold -inf outside each
+      // row's window; a lane stores the keys of the window (all keys with clean) below the unit's
+      // scored range on the chunk's pages.
+      __builtin_amdgcn_wave_barrier();
+      const int c0 = 4 * lane;
+      const int j0 = cur_pg * kPage + c0;
+      const bool page_live = c0 < cur_n * kPage;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const v4f x = *reinterpret_cast<const v4f*>(stage + r * kStageLd + c0);
+        const int len = t.len[r];
+        const bool rok = page_live && r < t.nq;
+        bool p[4];
+        bool all = true;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          p[c] = rok && j0 + c < covered && (j0 + c < len || clean);
+          all = all && p[c];
+        }
+        float* dst = a.logits + (int64_t)(r < t.nq ? t.r_base + r : 0) * a.ld + j0;
+        if (all) {
+          *reinterpret_cast<v4f*>(dst) = x;
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (p[c]) dst[c] = x[c];
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
     }
   }
 
@@ -289,7 +337,7 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
 
 void query_paged_occupancy(DeviceInfo& d) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, logits_paged_kernel<kPagedDepth>, 64 * kPagedWaves,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, logits_paged_kernel<kPagedDepth, true>, 64 * kPagedWaves,
                                                    0) != hipSuccess)
     per_cu = 1;
   d.paged_wgs_per_cu = per_cu > 0 ? per_cu : 1;
@@ -301,8 +349,13 @@ hipError_t launch_logits_paged(const PagedLogitsArgs& a, const DeviceInfo& dev, 
   if ((int64_t)a.B * qgroups > 0x7fffffffLL) return hipErrorInvalidValue;
   const int per_cu = dev.paged_wgs_per_cu > 0 ? dev.paged_wgs_per_cu : 1;
   const int64_t grid = (int64_t)(dev.cu_count > 0 ? dev.cu_count : 256) * per_cu;
-  hipLaunchKernelGGL(logits_paged_kernel<kPagedDepth>, dim3((unsigned)grid), dim3(64 * kPagedWaves), 0, s, a,
-                     qgroups);
+  const bool vec = (a.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL((logits_paged_kernel<kPagedDepth, true>), dim3((unsigned)grid), dim3(64 * kPagedWaves), 0, s,
+                       a, qgroups);
+  else
+    hipLaunchKernelGGL((logits_paged_kernel<kPagedDepth, false>), dim3((unsigned)grid), dim3(64 * kPagedWaves), 0, s,
+                       a, qgroups);
   return hipGetLastError();
 }
 

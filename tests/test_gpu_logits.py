@@ -318,3 +318,37 @@ def test_paged_equals_ragged_on_gathered_kv():
         torch.cuda.synchronize()
         # same per-(row, key) arithmetic, so the two forms agree bit for bit
         assert np.array_equal(gr.cpu().numpy(), g[rows, :n_b])
+
+
+@pytest.mark.parametrize("clean", [False, True])
+def test_paged_store_paths_agree(clean):
+    """The paged kernel stores a page's logits 16 bytes per lane when the rows are 16-byte aligned
+    and one key at a time otherwise.  Aligned rows, an odd row stride and a base 4 bytes past
+    alignment must give the same bits inside every window and the same contract outside it
+    (clean=0: nothing at or past row_len written; clean=1: -inf up to the width, nothing past it)."""
+    inp = paged_inputs(5, 4, 100, 1500, 16, seed=43, page_size=64)
+    width = inp.max_pages * 64 - 20        # not a whole number of pages
+    args = [to_dev(a) for a in (inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len, inp.block_table)]
+    o = paged_mqa_logits(inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len,
+                         inp.block_table, inp.page_size, width=width)
+    got = []
+    for ld, shift in ((width + 36, 0), (width + 33, 0), (width + 36, 1)):
+        flat = torch.full((inp.rows * ld + 4,), 12345.0, dtype=torch.float32, device="cuda")
+        out = flat[shift:shift + inp.rows * ld].view(inp.rows, ld)
+        F.indexer_logits_paged(*args, width=width, clean=clean, logits=out)
+        torch.cuda.synchronize()
+        g = out.cpu().numpy()
+        for r in range(inp.rows):
+            n = min(int(inp.row_len[r]), width)
+            d = np.abs(g[r, :n] - o[r, :n])
+            assert np.all(d <= 1e-3 + 2e-3 * np.abs(o[r, :n])), (ld, shift, r)
+            tail = g[r, n:width]
+            if clean:
+                assert np.all(tail == -np.inf), (ld, shift, r)
+            else:
+                assert np.all((tail == 12345.0) | (tail == -np.inf)), (ld, shift, r)
+            assert np.all(g[r, width:] == 12345.0), (ld, shift, r)
+        got.append([g[r, :min(int(inp.row_len[r]), width)].copy() for r in range(inp.rows)])
+    for other in got[1:]:
+        for a, b in zip(got[0], other):
+            assert np.array_equal(a, b)
