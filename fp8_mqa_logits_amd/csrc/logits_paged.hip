@@ -9,7 +9,7 @@
 // Work decomposition
 // - A unit is (request, group of 4 query rows); it owns ceil(L / 64) pages,
 //   L being the longest of its rows' lengths (clamped to the width), claimed
-//   in chunks of 4 pages.  The units' chunks, laid end to end, are split into
+//   in chunks of 8 pages.  The units' chunks, laid end to end, are split into
 //   equal contiguous ranges, one per workgroup of a persistent grid (one
 //   8-wave workgroup per CU), found by each workgroup with a wave-wide prefix
 //   scan of the chunk counts computed from the device-side lengths: no host
@@ -25,8 +25,8 @@
 //   boundaries.  Every kv byte is read once and is shared by the 4 query rows.
 // - Scoring, ReLU, head weighting and the cross-lane head reduction are the
 //   same register-resident core as the ragged kernel.
-// - A chunk's logits (4 rows x 4 pages) collect in the wave's LDS buffer and
-//   leave as one contiguous 1 KiB store per row (16 bytes per lane), when the
+// - A chunk's logits (4 rows x 8 pages) collect in the wave's LDS buffer and
+//   leave as contiguous 1 KiB stores per row (16 bytes per lane), when the
 //   rows are 16-byte aligned; otherwise each key is stored on its own.
 // - With clean set, keys past a unit's scored range are filled with -inf by a
 //   second balanced split over (unit, 64-key block) pairs.  Keys inside a
@@ -45,7 +45,7 @@ namespace fp8idx {
 constexpr int kPage = 64;
 constexpr int kPagedWaves = 8;         // one workgroup per CU (2 waves per SIMD)
 constexpr int kPagedDepth = 2;         // pages in flight per wave, the scored one included
-constexpr int kChunk = 4;              // pages a wave claims at a time
+constexpr int kChunk = 8;              // pages a wave claims at a time
 constexpr int kMinChunksPerWg = 2;     // small totals run on fewer workgroups
 constexpr int kFragsPerPage = kPage / 16;   // 16-key MFMA fragments per page
 constexpr int kStageLd = kChunk * kPage + 16;   // row stride of a wave's logits staging buffer (floats)
@@ -105,6 +105,7 @@ __device__ __forceinline__ int unit_chunks_at(const PagedLogitsArgs& a, int qgro
 
 static_assert(kPagedDepth == 2, "the chunk loop keeps one page in flight ahead of the scored one");
 static_assert(kChunk % kPagedDepth == 0, "chunks start on the first page buffer");
+static_assert(kChunk * kPage % 256 == 0, "a chunk's logits leave in 256-key slices, 4 keys per lane");
 
 // VEC_STORE: the logits rows are 16-byte aligned (ld a multiple of 4, base aligned), so a chunk's
 // logits go out as 16-byte stores, one contiguous 1 KiB per row (see below); otherwise as one
@@ -277,35 +278,38 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
       score_page(d, buf[d % DEPTH]);
     }
     if constexpr (VEC_STORE) {
-      // The chunk's logits leave the staging buffer as one contiguous 1 KiB store per row: lane l
-      // writes keys 4 l .. 4 l + 3 of the chunk.  LDS operations of one wave complete in order, so
+      // The chunk's logits leave the staging buffer in 256-key slices, one contiguous 1 KiB store
+      // per row and slice: lane l writes keys 4 l .. 4 l + 3 of the slice.  LDS operations of one wave complete in order, so
       // these reads see the chunk's writes and the next chunk's writes come after them; the wave
       // barriers keep the compiler from moving them.  Staged values already hold -inf outside each
       // row's window; a lane stores the keys of the window (all keys with clean) below the unit's
       // scored range on the chunk's pages.
       __builtin_amdgcn_wave_barrier();
-      const int c0 = 4 * lane;
-      const int j0 = cur_pg * kPage + c0;
-      const bool page_live = c0 < cur_n * kPage;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const v4f x = *reinterpret_cast<const v4f*>(stage + r * kStageLd + c0);
-        const int len = t.len[r];
-        const bool rok = page_live && r < t.nq;
-        bool p[4];
-        bool all = true;
+      for (int sl = 0; sl < kChunk * kPage; sl += 256) {
+        const int c0 = sl + 4 * lane;
+        const int j0 = cur_pg * kPage + c0;
+        const bool page_live = c0 < cur_n * kPage;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          p[c] = rok && j0 + c < covered && (j0 + c < len || clean);
-          all = all && p[c];
-        }
-        float* dst = a.logits + (int64_t)(r < t.nq ? t.r_base + r : 0) * a.ld + j0;
-        if (all) {
-          *reinterpret_cast<v4f*>(dst) = x;
-        } else {
+        for (int r = 0; r < 4; ++r) {
+          const v4f x = *reinterpret_cast<const v4f*>(stage + r * kStageLd + c0);
+          const int len = t.len[r];
+          const bool rok = page_live && r < t.nq;
+          bool p[4];
+          bool all = true;
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (p[c]) dst[c] = x[c];
+          for (int c = 0; c < 4; ++c) {
+            p[c] = rok && j0 + c < covered && (j0 + c < len || clean);
+            all = all && p[c];
+          }
+          float* dst = a.logits + (int64_t)(r < t.nq ? t.r_base + r : 0) * a.ld + j0;
+          if (all) {
+            *reinterpret_cast<v4f*>(dst) = x;
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (p[c]) dst[c] = x[c];
+          }
         }
       }
       __builtin_amdgcn_wave_barrier();
