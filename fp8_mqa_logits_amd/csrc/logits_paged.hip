@@ -9,7 +9,7 @@
 // Work decomposition
 // - A unit is (request, group of 4 query rows); it owns ceil(L / 64) pages,
 //   L being the longest of its rows' lengths (clamped to the width), claimed
-//   in chunks of 8 pages.  The units' chunks, laid end to end, are split into
+//   in chunks of 16 pages.  The units' chunks, laid end to end, are split into
 //   equal contiguous ranges, one per workgroup of a persistent grid (one
 //   8-wave workgroup per CU), found by each workgroup with a wave-wide prefix
 //   scan of the chunk counts computed from the device-side lengths: no host
@@ -25,9 +25,10 @@
 //   boundaries.  Every kv byte is read once and is shared by the 4 query rows.
 // - Scoring, ReLU, head weighting and the cross-lane head reduction are the
 //   same register-resident core as the ragged kernel.
-// - A chunk's logits (4 rows x 8 pages) collect in the wave's LDS buffer and
-//   leave as contiguous 1 KiB stores per row (16 bytes per lane), when the
-//   rows are 16-byte aligned; otherwise each key is stored on its own.
+// - A chunk's logits (4 rows x 16 pages) collect in the wave's LDS buffer and
+//   leave as contiguous 1 KiB stores, four per row, so each row receives an
+//   aligned 4 KiB block at once (16 bytes per lane), when the rows are 16-byte
+//   aligned; otherwise each key is stored on its own.
 // - With clean set, keys past a unit's scored range are filled with -inf by a
 //   second balanced split over (unit, 64-key block) pairs.  Keys inside a
 //   row's window whose page id lies outside the pool get -inf in any case.
@@ -45,7 +46,7 @@ namespace fp8idx {
 constexpr int kPage = 64;
 constexpr int kPagedWaves = 8;         // one workgroup per CU (2 waves per SIMD)
 constexpr int kPagedDepth = 2;         // pages in flight per wave, the scored one included
-constexpr int kChunk = 8;              // pages a wave claims at a time
+constexpr int kChunk = 16;             // pages a wave claims at a time
 constexpr int kMinChunksPerWg = 2;     // small totals run on fewer workgroups
 constexpr int kFragsPerPage = kPage / 16;   // 16-key MFMA fragments per page
 constexpr int kStageLd = kChunk * kPage + 16;   // row stride of a wave's logits staging buffer (floats)
