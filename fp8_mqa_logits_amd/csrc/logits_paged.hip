@@ -9,9 +9,9 @@
 // Work decomposition
 // - A unit is (request, group of 4 query rows); it owns ceil(L / 64) pages,
 //   L being the longest of its rows' lengths (clamped to the width), claimed
-//   in chunks of 16 pages.  The units' chunks, laid end to end, are split into
-//   equal contiguous ranges, one per workgroup of a persistent grid (one
-//   8-wave workgroup per CU), found by each workgroup with a wave-wide prefix
+//   in chunks of 16 pages (4 for small batches).  The units' chunks, laid end
+//   to end, are split into equal contiguous ranges, one per workgroup of a
+//   persistent grid (one 8-wave workgroup per CU), found by each workgroup with a wave-wide prefix
 //   scan of the chunk counts computed from the device-side lengths: no host
 //   schedule or workspace.  Inside a workgroup, waves take chunks from its
 //   range one at a time through an LDS counter.  Every CU gets the same work,
@@ -46,10 +46,14 @@ namespace fp8idx {
 constexpr int kPage = 64;
 constexpr int kPagedWaves = 8;         // one workgroup per CU (2 waves per SIMD)
 constexpr int kPagedDepth = 2;         // pages in flight per wave, the scored one included
-constexpr int kChunk = 16;             // pages a wave claims at a time
+// Pages a wave claims at a time: 16 when the grid has pages to spare (each row's logits then leave in
+// aligned 4 KiB blocks), 4 for small batches, whose few chunks would leave most waves idle.
+constexpr int kChunkLarge = 16;
+constexpr int kChunkSmall = 4;
+// The launcher takes the large chunk when the block tables can hold this many pages in total.
+constexpr int64_t kChunkLargeMinPages = 131072;
 constexpr int kMinChunksPerWg = 2;     // small totals run on fewer workgroups
 constexpr int kFragsPerPage = kPage / 16;   // 16-key MFMA fragments per page
-constexpr int kStageLd = kChunk * kPage + 16;   // row stride of a wave's logits staging buffer (floats)
 
 // One page's four B-operands (lane l: key l % 16 of each 16-key fragment,
 // bytes 32 * (l / 16) .. +32) and its 64 kv scales (lane l: key l).  The loads are unconditional (an
@@ -96,23 +100,26 @@ __device__ __forceinline__ Unit unit_at(const PagedLogitsArgs& a, int qgroups, i
   return t;
 }
 
-// Claimable chunks of unit u: its pages in runs of kChunk (the last run may be shorter).
-__device__ __forceinline__ int unit_chunks(const Unit& t) { return ((t.lmax + kPage - 1) / kPage + kChunk - 1) / kChunk; }
+// Claimable chunks of unit u: its pages in runs of CHUNK (the last run may be shorter).
+template <int CHUNK>
+__device__ __forceinline__ int unit_chunks(const Unit& t) { return ((t.lmax + kPage - 1) / kPage + CHUNK - 1) / CHUNK; }
 
+template <int CHUNK>
 __device__ __forceinline__ int unit_chunks_at(const PagedLogitsArgs& a, int qgroups, int units, int u) {
   if (u >= units) return 0;
-  return unit_chunks(unit_at(a, qgroups, u));
+  return unit_chunks<CHUNK>(unit_at(a, qgroups, u));
 }
 
 static_assert(kPagedDepth == 2, "the chunk loop keeps one page in flight ahead of the scored one");
-static_assert(kChunk % kPagedDepth == 0, "chunks start on the first page buffer");
-static_assert(kChunk * kPage % 256 == 0, "a chunk's logits leave in 256-key slices, 4 keys per lane");
 
 // VEC_STORE: the logits rows are 16-byte aligned (ld a multiple of 4, base aligned), so a chunk's
 // logits go out as 16-byte stores, one contiguous 1 KiB per row (see below); otherwise as one
 // 4-byte store per key.
-template <int DEPTH, bool VEC_STORE>
+template <int DEPTH, bool VEC_STORE, int CHUNK>
 __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(PagedLogitsArgs a, int qgroups) {
+  static_assert(CHUNK % kPagedDepth == 0, "chunks start on the first page buffer");
+  static_assert(CHUNK * kPage % 256 == 0, "a chunk's logits leave in 256-key slices, 4 keys per lane");
+  constexpr int kStageLd = CHUNK * kPage + 16;   // row stride of a wave's logits staging buffer (floats)
   __shared__ int s_next;   // next chunk of this workgroup's range to hand out
   // Per wave: one chunk's logits of the unit's 4 rows, rows kStageLd floats apart (16 floats of
   // padding keep the four rows' writes on different banks).
@@ -127,10 +134,10 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
   const int my_q = reduce_rows4_qsel(lane);
 
   // Total chunks over all units (the first 64 units' counts are kept for the search below).
-  const int c_first = unit_chunks_at(a, qgroups, units, lane);
+  const int c_first = unit_chunks_at<CHUNK>(a, qgroups, units, lane);
   int64_t total = __builtin_amdgcn_readfirstlane(wave_sum(c_first));
   for (int c = 64; c < units; c += 64)
-    total += __builtin_amdgcn_readfirstlane(wave_sum(unit_chunks_at(a, qgroups, units, c + lane)));
+    total += __builtin_amdgcn_readfirstlane(wave_sum(unit_chunks_at<CHUNK>(a, qgroups, units, c + lane)));
   total = uniform64(total);
 
   // This workgroup's equal share of the chunks.  Its waves take chunks from the share one at a time
@@ -148,7 +155,7 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
   if (ccount > 0) {
     int64_t run = 0;
     for (int c = 0; c < units; c += 64) {
-      const int p = c == 0 ? c_first : unit_chunks_at(a, qgroups, units, c + lane);
+      const int p = c == 0 ? c_first : unit_chunks_at<CHUNK>(a, qgroups, units, c + lane);
       const int incl = wave_inclusive_scan(p, lane);
       const int chunk = __builtin_amdgcn_readlane(incl, 63);
       if (c0 - run < chunk) {
@@ -162,7 +169,7 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
     }
   }
   Unit ct = unit_at(a, qgroups, min(cu, units - 1));
-  int ct_chunks = unit_chunks(ct);
+  int ct_chunks = unit_chunks<CHUNK>(ct);
 
   // Claims the next chunk: its unit, first page, page count (0: none left) and page ids (lane l:
   // page l, lanes past the count repeat the last one).  The id load is unconditional (entry 0 of the
@@ -182,11 +189,11 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
         cstart += ct_chunks;
         ++cu;
         ct = unit_at(a, qgroups, cu);
-        ct_chunks = unit_chunks(ct);
+        ct_chunks = unit_chunks<CHUNK>(ct);
       }
       nx_u = cu;
-      nx_pg = (int)(c - cstart) * kChunk;
-      nx_n = min(kChunk, (ct.lmax + kPage - 1) / kPage - nx_pg);
+      nx_pg = (int)(c - cstart) * CHUNK;
+      nx_n = min(CHUNK, (ct.lmax + kPage - 1) / kPage - nx_pg);
       idx = (int64_t)ct.b * a.max_pages + nx_pg + min(lane, nx_n - 1);
     }
     nx_ids = a.block_table[idx];
@@ -269,9 +276,9 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
     // One page loads while the previous one is scored; the chunk's last step
     // loads the next chunk's first page.
 #pragma unroll
-    for (int d = 0; d < kChunk; ++d) {
+    for (int d = 0; d < CHUNK; ++d) {
       int32_t np;
-      if (d + 1 < kChunk)
+      if (d + 1 < CHUNK)
         np = d + 1 < cur_n ? __builtin_amdgcn_readlane(cur_pidv, d + 1) : -1;
       else
         np = nx_n > 0 ? __builtin_amdgcn_readfirstlane(nx_ids) : -1;
@@ -287,7 +294,7 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
       // scored range on the chunk's pages.
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int sl = 0; sl < kChunk * kPage; sl += 256) {
+      for (int sl = 0; sl < CHUNK * kPage; sl += 256) {
         const int c0 = sl + 4 * lane;
         const int j0 = cur_pg * kPage + c0;
         const bool page_live = c0 < cur_n * kPage;
@@ -342,7 +349,8 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
 
 void query_paged_occupancy(DeviceInfo& d) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, logits_paged_kernel<kPagedDepth, true>, 64 * kPagedWaves,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, logits_paged_kernel<kPagedDepth, true, kChunkLarge>,
+                                                   64 * kPagedWaves,
                                                    0) != hipSuccess)
     per_cu = 1;
   d.paged_wgs_per_cu = per_cu > 0 ? per_cu : 1;
@@ -355,12 +363,18 @@ hipError_t launch_logits_paged(const PagedLogitsArgs& a, const DeviceInfo& dev, 
   const int per_cu = dev.paged_wgs_per_cu > 0 ? dev.paged_wgs_per_cu : 1;
   const int64_t grid = (int64_t)(dev.cu_count > 0 ? dev.cu_count : 256) * per_cu;
   const bool vec = (a.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
-  if (vec)
-    hipLaunchKernelGGL((logits_paged_kernel<kPagedDepth, true>), dim3((unsigned)grid), dim3(64 * kPagedWaves), 0, s,
-                       a, qgroups);
+  // pages the block tables can name: every unit's rows clamped to the table and the width
+  const int64_t table_pages = std::min<int64_t>(a.max_pages, ((int64_t)a.width + kPage - 1) / kPage);
+  const bool large = (int64_t)a.B * qgroups * table_pages >= kChunkLargeMinPages;
+  const dim3 g((unsigned)grid), blk(64 * kPagedWaves);
+  if (vec && large)
+    hipLaunchKernelGGL((logits_paged_kernel<kPagedDepth, true, kChunkLarge>), g, blk, 0, s, a, qgroups);
+  else if (vec)
+    hipLaunchKernelGGL((logits_paged_kernel<kPagedDepth, true, kChunkSmall>), g, blk, 0, s, a, qgroups);
+  else if (large)
+    hipLaunchKernelGGL((logits_paged_kernel<kPagedDepth, false, kChunkLarge>), g, blk, 0, s, a, qgroups);
   else
-    hipLaunchKernelGGL((logits_paged_kernel<kPagedDepth, false>), dim3((unsigned)grid), dim3(64 * kPagedWaves), 0, s,
-                       a, qgroups);
+    hipLaunchKernelGGL((logits_paged_kernel<kPagedDepth, false, kChunkSmall>), g, blk, 0, s, a, qgroups);
   return hipGetLastError();
 }
 

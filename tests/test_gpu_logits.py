@@ -352,3 +352,47 @@ def test_paged_store_paths_agree(clean):
     for other in got[1:]:
         for a, b in zip(got[0], other):
             assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("clean", [False, True])
+def test_paged_large_chunk_path(clean):
+    """Block tables that can name at least 131072 pages in total take 16-page chunks; smaller ones
+    take 4-page chunks.  128 one-row requests with a 1024-page table and a 65536-key width take the
+    large chunks (aligned rows and an odd stride, so both store forms); the same rows over a
+    narrower table take the small chunks.  Every row against the oracle, and the in-window bits of
+    all forms equal."""
+    B = 128
+    inp = paged_inputs(B, 1, 100, 3000, 16, seed=44, page_size=64)
+    bt = np.full((B, 1024), -1, dtype=np.int32)
+    bt[:, :inp.block_table.shape[1]] = inp.block_table
+    width = 1024 * 64
+    args = [to_dev(a) for a in (inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len, bt)]
+    o = paged_mqa_logits(inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len,
+                         inp.block_table, inp.page_size, width=int(inp.row_len.max()))
+    got = []
+    for ld in (width, width + 33):
+        out = torch.full((inp.rows, ld), 12345.0, dtype=torch.float32, device="cuda")
+        F.indexer_logits_paged(*args, width=width, clean=clean, logits=out)
+        torch.cuda.synchronize()
+        g = out.cpu().numpy()
+        for r in range(inp.rows):
+            n = int(inp.row_len[r])
+            d = np.abs(g[r, :n] - o[r, :n])
+            assert np.all(d <= 1e-3 + 2e-3 * np.abs(o[r, :n])), (ld, r)
+            tail = g[r, n:width]
+            if clean:
+                assert np.all(tail == -np.inf), (ld, r)
+            else:
+                assert np.all((tail == 12345.0) | (tail == -np.inf)), (ld, r)
+            assert np.all(g[r, width:] == 12345.0), (ld, r)
+        got.append(g)
+    # the narrow table (the requests' own pages only) runs the 4-page chunks
+    narrow = inp.block_table.shape[1] * 64
+    small = F.indexer_logits_paged(*[to_dev(a) for a in (inp.q, inp.kv_pool, inp.scale_pool, inp.weights,
+                                                        inp.row_len, inp.block_table)], width=narrow, clean=clean)
+    torch.cuda.synchronize()
+    s = small.cpu().numpy()
+    for r in range(inp.rows):
+        n = int(inp.row_len[r])
+        assert np.array_equal(got[0][r, :n], got[1][r, :n]), r
+        assert np.array_equal(got[0][r, :n], s[r, :n]), r
