@@ -113,8 +113,8 @@ __device__ __forceinline__ int unit_chunks_at(const PagedLogitsArgs& a, int qgro
 static_assert(kPagedDepth == 2, "the chunk loop keeps one page in flight ahead of the scored one");
 
 // VEC_STORE: the logits rows are 16-byte aligned (ld a multiple of 4, base aligned), so a chunk's
-// logits go out as 16-byte stores, CHUNK / 4 contiguous 1 KiB stores per row (see below); otherwise
-// as one 4-byte store per key.  CHUNK: pages per claimed chunk (kChunkLarge or kChunkSmall).
+// logits go out as 16-byte stores, one contiguous 1 KiB per row (see below); otherwise as one
+// 4-byte store per key.
 template <int DEPTH, bool VEC_STORE, int CHUNK>
 __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(PagedLogitsArgs a, int qgroups) {
   static_assert(CHUNK % kPagedDepth == 0, "chunks start on the first page buffer");
