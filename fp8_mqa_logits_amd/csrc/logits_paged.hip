@@ -11,9 +11,9 @@
 //   L being the longest of its rows' lengths (clamped to the width), claimed
 //   in chunks of 16 pages (4 for small batches).  The units' chunks, laid end
 //   to end, are split into equal contiguous ranges, one per workgroup of a
-//   persistent grid (one 8-wave workgroup per CU), found by each workgroup with a wave-wide prefix
-//   scan of the chunk counts computed from the device-side lengths: no host
-//   schedule or workspace.  Inside a workgroup, waves take chunks from its
+//   persistent grid (one 8-wave workgroup per CU), found by each workgroup
+//   with a wave-wide prefix scan of the chunk counts computed from the
+//   device-side lengths: no host schedule or workspace.  Inside a workgroup, waves take chunks from its
 //   range one at a time through an LDS counter.  Every CU gets the same work,
 //   and a wave that its SIMD serves less often (issue favours older waves)
 //   simply takes fewer chunks, so the waves finish together.
@@ -113,8 +113,8 @@ __device__ __forceinline__ int unit_chunks_at(const PagedLogitsArgs& a, int qgro
 static_assert(kPagedDepth == 2, "the chunk loop keeps one page in flight ahead of the scored one");
 
 // VEC_STORE: the logits rows are 16-byte aligned (ld a multiple of 4, base aligned), so a chunk's
-// logits go out as 16-byte stores, one contiguous 1 KiB per row (see below); otherwise as one
-// 4-byte store per key.
+// logits go out as 16-byte stores, CHUNK / 4 contiguous 1 KiB stores per row (see below); otherwise
+// as one 4-byte store per key.  CHUNK: pages per claimed chunk (kChunkLarge or kChunkSmall).
 template <int DEPTH, bool VEC_STORE, int CHUNK>
 __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(PagedLogitsArgs a, int qgroups) {
   static_assert(CHUNK % kPagedDepth == 0, "chunks start on the first page buffer");
@@ -287,9 +287,9 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
     }
     if constexpr (VEC_STORE) {
       // The chunk's logits leave the staging buffer in 256-key slices, one contiguous 1 KiB store
-      // per row and slice: lane l writes keys 4 l .. 4 l + 3 of the slice.  LDS operations of one wave complete in order, so
-      // these reads see the chunk's writes and the next chunk's writes come after them; the wave
-      // barriers keep the compiler from moving them.  Staged values already hold -inf outside each
+      // per row and slice: lane l writes keys 4 l .. 4 l + 3 of the slice.  LDS operations of one
+      // wave complete in order, so these reads see the chunk's writes and the next chunk's writes
+      // come after them; the wave barriers keep the compiler from moving them.  Staged values already hold -inf outside each
       // row's window; a lane stores the keys of the window (all keys with clean) below the unit's
       // scored range on the chunk's pages.
       __builtin_amdgcn_wave_barrier();
@@ -350,8 +350,7 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
 void query_paged_occupancy(DeviceInfo& d) {
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, logits_paged_kernel<kPagedDepth, true, kChunkLarge>,
-                                                   64 * kPagedWaves,
-                                                   0) != hipSuccess)
+                                                   64 * kPagedWaves, 0) != hipSuccess)
     per_cu = 1;
   d.paged_wgs_per_cu = per_cu > 0 ? per_cu : 1;
 }
