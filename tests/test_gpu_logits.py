@@ -396,3 +396,35 @@ def test_paged_large_chunk_path(clean):
         n = int(inp.row_len[r])
         assert np.array_equal(got[0][r, :n], got[1][r, :n]), r
         assert np.array_equal(got[0][r, :n], s[r, :n]), r
+
+
+@pytest.mark.parametrize("clean", [False, True])
+def test_paged_large_chunk_path_many_units_and_empty_rows(clean):
+    """The 16-page chunks with several units per request (next_n 6: a 4-row unit and a 2-row unit)
+    and empty and one-key contexts mixed in; every row against the oracle."""
+    B, nn = 70, 6
+    rng = np.random.default_rng(45)
+    ctx = rng.integers(0, 900, B)
+    ctx[rng.random(B) < 0.2] = 0
+    ctx[::13] = 1
+    ctx[0] = 900
+    inp = paged_inputs(B, nn, 0, 900, 16, seed=46, page_size=64, ctx=ctx)
+    bt = np.full((B, 1024), -1, dtype=np.int32)
+    bt[:, :inp.block_table.shape[1]] = inp.block_table
+    width = 1024 * 64   # 70 requests x 2 units x 1024 table pages >= 131072: 16-page chunks
+    args = [to_dev(a) for a in (inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len, bt)]
+    out = torch.full((inp.rows, width), 12345.0, dtype=torch.float32, device="cuda")
+    F.indexer_logits_paged(*args, width=width, clean=clean, logits=out)
+    torch.cuda.synchronize()
+    g = out.cpu().numpy()
+    o = paged_mqa_logits(inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len,
+                         inp.block_table, inp.page_size, width=max(1, int(inp.row_len.max())))
+    for r in range(inp.rows):
+        n = int(inp.row_len[r])
+        d = np.abs(g[r, :n] - o[r, :n])
+        assert np.all(d <= 1e-3 + 2e-3 * np.abs(o[r, :n])), r
+        tail = g[r, n:]
+        if clean:
+            assert np.all(tail == -np.inf), r
+        else:
+            assert np.all((tail == 12345.0) | (tail == -np.inf)), r
