@@ -86,6 +86,9 @@ def _args():
     ap.add_argument("--trace-summary", default="", metavar="CSV")
     ap.add_argument("--all-workloads", default="")
     ap.add_argument("--overlap", action="store_true", help="time the fused loop serial vs overlapped")
+    ap.add_argument("--cap-sweep", action="store_true",
+                    help="the chunking page's experiment: fused step per logits cap (0 = one shot), serial and "
+                         "overlapped, on the 8192 x 65536 and long-prefix workloads")
     ap.add_argument("--prep", action="store_true", help="time index preparation at the PR page's shapes")
     ap.add_argument("--quant", action="store_true", help="time the fp8 quantiser on the path's kv and q shapes")
     ap.add_argument("--sparse-mla", action="store_true",
@@ -532,6 +535,46 @@ def run_workload(name, steps, warmup, cold=False, overlap=False):
     return res
 
 
+# Logits caps of the chunking page's experiment (bytes; 0 = one shot, the whole rows x keys buffer).
+CAP_SWEEP = (0, 8_000_000_000, 4_000_000_000, 2_000_000_000, 1_000_000_000, 500_000_000)
+
+
+def cap_sweep(steps, warmup):
+    """The fused logits + top-k step per logits cap, serial and with chunk N - 1's top-k overlapped
+    (the chunking page's `main`: ms per layer per cap against the one-shot run).  Every cap's selection
+    is compared with the one-shot selection: the per-(row, key) arithmetic does not depend on the
+    chunking, so the selected sets must be equal."""
+    import dataclasses
+    import numpy as np
+    import torch
+    from workloads.generate import config_inputs
+    out = []
+    for name in ("prefill_64k", "long_prefix_210k"):
+        base = config_inputs(name)
+        one_shot, ref = None, None
+        for cap in CAP_SWEEP:
+            inp = dataclasses.replace(base, cap_bytes=cap)
+            step = RaggedStep(inp)
+            chunks = -(-inp.m // step.rpc)
+            serial, _ = _time_fused(step, steps, warmup)
+            sel = np.sort(step.out.cpu().numpy(), axis=1)
+            if ref is None:
+                ref, one_shot = sel, serial
+            r = {"workload": base.name.split("_cap")[0], "cap_gb": cap / 1e9, "chunks": chunks,
+                 "rows_per_chunk": step.rpc, "peak_logits_mb": round(step.rpc * step.ld * 4 / 1e6, 1),
+                 "serial_ms": round(serial, 4), "vs_one_shot": round(serial / one_shot - 1, 4),
+                 "selection_equal_one_shot": bool(np.array_equal(sel, ref))}
+            if chunks > 1:
+                over, _ = _time_fused(step, steps, warmup, overlap=True)
+                r["overlap_ms"] = round(over, 4)
+                r["overlap_selection_equal_one_shot"] = bool(
+                    np.array_equal(np.sort(step.out.cpu().numpy(), axis=1), ref))
+            out.append(r)
+            del step
+            torch.cuda.empty_cache()
+    return out
+
+
 QUANT_SHAPES = (
     ("kv_n65536_d128", 65536, 128),          # the 65536-key prefill's kv (per-token scales)
     ("q_m8192_h32_d128", 8192 * 32, 128),    # its q, one row per (query row, head)
@@ -858,6 +901,10 @@ def main():
                               "overlap_gain": round(serial / over - 1, 4)}), flush=True)
             del step, inp
             torch.cuda.empty_cache()
+        return
+    if a.cap_sweep:
+        for r in cap_sweep(a.steps, a.warmup):
+            print(json.dumps(r), flush=True)
         return
     if a.prep:
         for q in prep_workloads(a.steps, a.warmup):
