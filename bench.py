@@ -88,7 +88,7 @@ def _args():
     ap.add_argument("--overlap", action="store_true", help="time the fused loop serial vs overlapped")
     ap.add_argument("--cap-sweep", action="store_true",
                     help="the chunking page's experiment: fused step per logits cap (0 = one shot), serial and "
-                         "overlapped, on the 8192 x 65536 and long-prefix workloads")
+                         "overlapped, on the page's four scenarios")
     ap.add_argument("--prep", action="store_true", help="time index preparation at the PR page's shapes")
     ap.add_argument("--quant", action="store_true", help="time the fp8 quantiser on the path's kv and q shapes")
     ap.add_argument("--sparse-mla", action="store_true",
@@ -549,7 +549,7 @@ def cap_sweep(steps, warmup):
     import torch
     from workloads.generate import config_inputs
     out = []
-    for name in ("prefill_64k", "long_prefix_210k"):
+    for name in ("prefill_64k", "tail_80k", "warm_154k", "long_prefix_210k"):
         base = config_inputs(name)
         one_shot, ref = None, None
         for cap in CAP_SWEEP:

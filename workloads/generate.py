@@ -286,6 +286,16 @@ def _long210k() -> RaggedInputs:
                          cap_bytes=2_000_000_000)
 
 
+def _tail80k() -> RaggedInputs:
+    # 80K_tail_chunk_14K of the chunking page: prefix 65536, extend 14464 -> m = 1808, n = 80000
+    return ragged_inputs(1808, 80000, 2048, seed=6, name="prefill_m1808_n80000")
+
+
+def _warm154k() -> RaggedInputs:
+    # warm_cont_150K+4K of the chunking page: prefix 150000, extend 4096 -> m = 512, n = 154096
+    return ragged_inputs(512, 154096, 2048, seed=7, name="prefill_m512_n154096")
+
+
 CONFIGS: Dict[str, Callable[[], object]] = {
     "tiny": _tiny,
     "prefill_64k": _cold64k,
@@ -293,6 +303,8 @@ CONFIGS: Dict[str, Callable[[], object]] = {
     "paged_decode": _paged,
     "paged_decode_sequential": _paged_sequential,
     "long_prefix_210k": _long210k,
+    "tail_80k": _tail80k,
+    "warm_154k": _warm154k,
 }
 
 
