@@ -124,8 +124,10 @@ def _sample_rows(m, chunk):
     return sorted(r for r in rows if 0 <= r < m)
 
 
-@pytest.mark.parametrize("name", ["tiny", "prefill_35k", "prefill_64k", "long_prefix_210k"])
+@pytest.mark.parametrize("name", ["tiny", "prefill_35k", "prefill_64k", "long_prefix_210k", "tail_80k", "warm_154k"])
 def test_full_size_ragged_configs_sampled(name):
+    """Sampled rows of each ragged workload through the fused entry at its cap (tail_80k and warm_154k:
+    the chunking page's other two scenarios, one shot) against the float64 oracle."""
     inp = config_inputs(name)
     d = _dev(inp)
     cap = inp.cap_bytes
