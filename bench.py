@@ -78,7 +78,7 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the on-box MFMA and copy peak probes")
     ap.add_argument("--cold", action="store_true",
-                    help="rewrite a 512 MiB scratch buffer before each timed step (cold caches)")
+                    help="read a 512 MiB scratch buffer before each timed step (cold, clean caches)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--core-probe", type=int, default=0, metavar="LAUNCHES",
@@ -284,16 +284,32 @@ def _roctx():
     return ROCTX
 
 
+def _scratch():
+    """512 MiB of device memory for evicting the caches (twice the 256 MB Infinity Cache)."""
+    import torch
+    x = torch.zeros((512 << 20) // 4, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    return x
+
+
+def _evict(scratch):
+    """Evict the caches by reading the scratch buffer: the lines it leaves are clean, so the step
+    that follows pays no write-backs for them (rewriting the buffer instead would leave up to 256 MB
+    of dirty lines whose write-backs land inside the step)."""
+    scratch.sum()
+
+
 def _time_steps(step, steps, warmup, record, cold=False):
     """Wall ms per step over `steps` timed steps of the launches made one call at a time; with
     record, per-launch and per-step HIP events (on the launch stream) are kept on the step for the
     kernel times and the step distribution.
 
-    cold: before every step a 512 MiB scratch buffer is rewritten (more than the 256 MB Infinity
-    Cache), so each step starts with cold caches; the flush lies outside the step events, and the
-    returned ms per step is then the mean of the step events instead of the wall time."""
+    cold: before every step a 512 MiB scratch buffer is read (more than the 256 MB Infinity Cache),
+    so each step starts with caches holding none of its data (see _evict); the flush lies outside
+    the step events, and the returned ms per step is then the mean of the step events instead of the
+    wall time."""
     import torch
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if cold else None
+    scratch = _scratch() if cold else None
     for _ in range(warmup):
         step.run()
     torch.cuda.synchronize()
@@ -303,7 +319,7 @@ def _time_steps(step, steps, warmup, record, cold=False):
     t0 = time.perf_counter()
     for i in range(steps):
         if cold:
-            scratch.fill_(i & 0xff)
+            _evict(scratch)
         if record:
             se = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             se[0].record()
@@ -412,10 +428,10 @@ def _time_fused(step, steps, warmup, overlap=False, cold=False):
     one).  The timed loop holds the calls alone, between two synchronisations: a timing event pair
     recorded inside every step costs GPU time of its own (about 13 us per step, 7% of a decode step).
     The per-step distribution comes from a second loop of `steps` calls, each bracketed by events.
-    With `cold`, a scratch fill between steps evicts the caches and the step times are those events."""
+    With `cold`, a scratch read between steps evicts the caches and the step times are those events."""
     import torch
     run = step.run_overlap if overlap else step.run_fused
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if cold else None
+    scratch = _scratch() if cold else None
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -431,7 +447,7 @@ def _time_fused(step, steps, warmup, overlap=False, cold=False):
     evs = []
     for i in range(steps):
         if cold:
-            scratch.fill_(i & 0xff)
+            _evict(scratch)
         e = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
         e[0].record()
         run()

@@ -158,7 +158,7 @@ struct FusedLayout {
   size_t queue_bytes;   // work-queue counters of the ragged logits launches
   size_t buf_bytes;     // one chunk of logits
   int32_t buffers;      // chunk logits buffers (2 when the overlap entry alternates them)
-  int64_t ld_frag;      // fragment maxima per row (16-key fragments of the width)
+  int64_t frag_elems;   // fragment maxima of one chunk's requests (any chunk size of the paged kernel)
   size_t frag_bytes;    // one chunk's fragment maxima (paged, one-workgroup-per-row top-k), else 0
   size_t topk_bytes;    // candidates of the largest chunk's top-k
   size_t total;
@@ -187,9 +187,13 @@ FusedLayout fused_layout(int32_t rows, int64_t width, int32_t k, size_t cap, int
   L.queue_bytes = ragged ? fp8idx::kRaggedQueueBytes : 0;
   L.buf_bytes = align256((size_t)rpc * (size_t)ld * 4u);
   L.buffers = rpc < rows ? logit_buffers : 1;
-  L.ld_frag = (width + 15) / 16;
+  // the paged kernel's chunk-major maxima: per 4-row unit, min(4, next_n) rows of every 16-key
+  // fragment of the width, rounded up to whole chunks of the larger chunk size (16 pages)
+  const int32_t nn = std::max(granule, 1);
+  const int64_t units = (int64_t)(rpc / nn) * ((nn + 3) / 4);
+  L.frag_elems = units * ((width + 1023) / 1024) * (int64_t)std::min(4, nn) * 64;
   const bool frag = !ragged && (fp8idx::topk_plan_takes_frag_max(p0) || fp8idx::topk_plan_takes_frag_max(p1));
-  L.frag_bytes = frag ? align256((size_t)rpc * (size_t)L.ld_frag * 4u) : 0;
+  L.frag_bytes = frag ? align256((size_t)L.frag_elems * 4u) : 0;
   L.topk_bytes = std::max(fp8idx::topk_workspace_bytes(p0), fp8idx::topk_workspace_bytes(p1));
   L.total = L.queue_bytes + L.buf_bytes * (size_t)L.buffers + L.frag_bytes + L.topk_bytes;
   return L;
@@ -710,13 +714,15 @@ fp8idx_status indexer_logits_topk_paged(const uint8_t* q, const uint8_t* kv_pool
     // per-fragment maxima
     const fp8idx::TopkPlan plan = fp8idx::plan_topk(nr, width, k);
     uint32_t* fm = fp8idx::topk_plan_takes_frag_max(plan) ? frag_max : nullptr;
+    fp8idx::FragLayout fl = fp8idx::paged_frag_layout(nb, next_n, max_pages, width);
+    fl.elems = L.frag_elems;
     fp8idx::PagedLogitsArgs la{q + (size_t)r0 * fp8idx::kQRowBytesHost, kv_pool, scale_pool,
                                weights + (size_t)r0 * 32, row_len + r0, block_table + (int64_t)b0 * max_pages,
-                               nb, next_n, max_pages, num_pages, chunk_logits, ld, width, 0, fm, L.ld_frag};
+                               nb, next_n, max_pages, num_pages, chunk_logits, ld, width, 0, fm, fl};
     hipError_t e = fp8idx::launch_logits_paged(la, dev, st);
     if (e != hipSuccess) return hip_fail(e);
     fp8idx::TopkArgs ta{chunk_logits, ld, nr, width, nullptr, row_len + r0, k, r0, kmap,
-                        out + (int64_t)r0 * ld_out, ld_out, fm, L.ld_frag};
+                        out + (int64_t)r0 * ld_out, ld_out, fm, fl, next_n};
     e = fp8idx::launch_topk(ta, plan, topk_ws, st);
     if (e != hipSuccess) return hip_fail(e);
   }

@@ -29,6 +29,19 @@ struct RaggedLogitsArgs {
 constexpr int kRaggedQueueWords = 8;
 constexpr size_t kRaggedQueueBytes = 256;
 
+// Layout of the paged logits kernel's per-fragment maxima (the fused paged entry hands them to its
+// top-k).  Chunk-major, so that each claimed chunk's maxima leave as one contiguous block: the
+// maxima of unit u's chunk c are frag_max[u * unit_stride + c * rows * fpc + r * fpc + j] for the
+// unit's row r < rows and the chunk's 16-key fragment j < fpc; fragment f of a row is chunk f / fpc,
+// j = f % fpc.  A row's request b and index t (of next_n) give u = b * ceil(next_n / 4) + t / 4,
+// r = t % 4.
+struct FragLayout {
+  int32_t rows;          // row slots per block: min(4, next_n)
+  int32_t fpc;           // fragments per row and chunk: 4 x the chunk's pages
+  int64_t unit_stride;   // elements per unit: blocks for every chunk of the width
+  int64_t elems;         // capacity of frag_max (elements), checked by every store
+};
+
 struct PagedLogitsArgs {
   const uint8_t* q;
   const uint8_t* kv_pool;
@@ -45,10 +58,11 @@ struct PagedLogitsArgs {
   int32_t width;
   int32_t clean;
   // Optional (null: not written): per (row, 16-key fragment f) the largest order code
-  // (float_to_ordered) of the row's logits at keys [16 f, 16 f + 16) inside its window, at
-  // frag_max[row * ld_frag + f], for every fragment that holds a key of the row's window.
+  // (float_to_ordered) of the row's logits at keys [16 f, 16 f + 16) inside its window (0 for none),
+  // laid out as `frag` says (take it from paged_frag_layout for the same B, next_n, max_pages and
+  // width); only with 16-byte aligned logits rows and frag_max.
   uint32_t* frag_max;
-  int64_t ld_frag;
+  FragLayout frag;
 };
 
 struct TopkMap {
@@ -75,9 +89,11 @@ struct TopkArgs {
   int32_t* out;
   int64_t ld_out;
   // Optional: the fragment maxima the paged logits kernel wrote for these logits (see
-  // PagedLogitsArgs::frag_max); used by the one-workgroup-per-row configuration when ks is null.
+  // PagedLogitsArgs::frag_max), row i of the call being row i of that launch, whose requests have
+  // frag_next_n rows; used by the one-workgroup-per-row configuration when ks is null.
   const uint32_t* frag_max;
-  int64_t ld_frag;
+  FragLayout frag;
+  int32_t frag_next_n;
 };
 
 // Host-side plan of the multi-level top-k: level 0 splits each row into
@@ -122,6 +138,9 @@ hipError_t launch_logits_ragged(const RaggedLogitsArgs& a, const DeviceInfo& dev
 // once per device; used by the entry point that allocates nothing.
 hipError_t ragged_noalloc_queue(unsigned int** out);
 hipError_t launch_logits_paged(const PagedLogitsArgs& a, const DeviceInfo& dev, hipStream_t s);
+// The fragment-maxima layout a paged logits launch over B requests of next_n rows uses (elems = 0:
+// the caller sets the capacity).
+FragLayout paged_frag_layout(int32_t B, int32_t next_n, int32_t max_pages, int32_t width);
 constexpr int kPrepMaxReq = 4096;   // requests per index-preparation call
 struct PrepRaggedArgs {
   const int32_t* seq_len;

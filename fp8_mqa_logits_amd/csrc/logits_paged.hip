@@ -43,6 +43,8 @@
 
 namespace fp8idx {
 
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
 constexpr int kPage = 64;
 constexpr int kPagedWaves = 8;         // one workgroup per CU (2 waves per SIMD)
 constexpr int kPagedDepth = 2;         // pages in flight per wave, the scored one included
@@ -124,6 +126,8 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
   // Per wave: one chunk's logits of the unit's 4 rows, rows kStageLd floats apart (16 floats of
   // padding keep the four rows' writes on different banks).
   __shared__ float s_stage[kPagedWaves][4 * kStageLd];
+  // Per wave: the chunk's fragment maxima of the unit's 4 rows (rows 4 * CHUNK apart, as they leave).
+  __shared__ uint32_t s_fstage[kPagedWaves][4 * 4 * CHUNK];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -209,6 +213,7 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
   bool row_ok = false;
   float* __restrict__ out_row = a.logits;
   float* const stage = s_stage[wave];
+  uint32_t* const fstage = s_fstage[wave];
 
   while (nx_n > 0) {
     // the claimed chunk becomes the current one; the cursor still sits on its unit
@@ -264,13 +269,14 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
         // the fragment's largest in-window code for the top-k (0 for keys outside the window)
         if (a.frag_max) fmax[f] = row16_max_u32(live && row_ok && inwin ? float_to_ordered(st) : 0u);
       }
-      if (a.frag_max) {
-        // lanes 0..3 of each 16-lane row store that row's four fragment maxima of this page
-        const int c = lane & 15;
-        const int64_t fidx = (int64_t)(cur_pg + i) * kFragsPerPage + c;
-        const uint32_t m = c == 0 ? fmax[0] : c == 1 ? fmax[1] : c == 2 ? fmax[2] : fmax[3];
-        if (live && row_ok && c < kFragsPerPage && fidx < a.ld_frag && fidx * 16 < covered)
-          a.frag_max[(int64_t)(t.r_base + my_q) * a.ld_frag + fidx] = m;
+      if constexpr (VEC_STORE) {
+        if (a.frag_max) {
+          // lanes 0..3 of each 16-lane row stage that row's four fragment maxima of this page
+          // (0 past the chunk's pages, past the row's window and for rows the unit lacks)
+          const int c = lane & 15;
+          const uint32_t m = c == 0 ? fmax[0] : c == 1 ? fmax[1] : c == 2 ? fmax[2] : fmax[3];
+          if (c < kFragsPerPage) fstage[my_q * (4 * CHUNK) + i * kFragsPerPage + c] = m;
+        }
       }
     };
     // One page loads while the previous one is scored; the chunk's last step
@@ -320,6 +326,16 @@ __global__ __launch_bounds__(64 * kPagedWaves, 1) void logits_paged_kernel(Paged
           }
         }
       }
+      if (a.frag_max) {
+        // the chunk's maxima block (a.frag.rows rows of 4 * CHUNK fragments, contiguous): lane l
+        // writes elements 4 l .. 4 l + 3
+        const int blk = a.frag.rows * (4 * CHUNK);
+        if (4 * lane < blk) {
+          const v4u x = *reinterpret_cast<const v4u*>(fstage + 4 * lane);
+          const int64_t idx = (int64_t)q_u * a.frag.unit_stride + (int64_t)(cur_pg / CHUNK) * blk + 4 * lane;
+          if (idx + 4 <= a.frag.elems) *reinterpret_cast<v4u*>(a.frag_max + idx) = x;
+        }
+      }
       __builtin_amdgcn_wave_barrier();
     }
   }
@@ -355,6 +371,27 @@ void query_paged_occupancy(DeviceInfo& d) {
   d.paged_wgs_per_cu = per_cu > 0 ? per_cu : 1;
 }
 
+// Pages per claimed chunk: the large chunk when the block tables can name at least
+// kChunkLargeMinPages pages in all (every unit's rows clamped to the table and the width).
+static int chunk_pages(int32_t B, int qgroups, int32_t max_pages, int32_t width) {
+  const int64_t table_pages = std::min<int64_t>(max_pages, ((int64_t)width + kPage - 1) / kPage);
+  return (int64_t)B * qgroups * table_pages >= kChunkLargeMinPages ? kChunkLarge : kChunkSmall;
+}
+
+static int chunk_pages(const PagedLogitsArgs& a, int qgroups) { return chunk_pages(a.B, qgroups, a.max_pages, a.width); }
+
+FragLayout paged_frag_layout(int32_t B, int32_t next_n, int32_t max_pages, int32_t width) {
+  FragLayout f{};
+  const int qgroups = (next_n + 3) / 4;
+  const int chunk = chunk_pages(B, qgroups, max_pages, width);
+  const int64_t pages = ((int64_t)std::max(width, 0) + kPage - 1) / kPage;
+  f.rows = std::min(4, std::max(next_n, 1));
+  f.fpc = 4 * chunk;
+  f.unit_stride = (pages + chunk - 1) / chunk * (int64_t)f.rows * f.fpc;
+  f.elems = 0;
+  return f;
+}
+
 hipError_t launch_logits_paged(const PagedLogitsArgs& a, const DeviceInfo& dev, hipStream_t s) {
   if (a.B <= 0 || a.width <= 0) return hipSuccess;
   const int qgroups = (a.next_n + 3) / 4;
@@ -362,9 +399,11 @@ hipError_t launch_logits_paged(const PagedLogitsArgs& a, const DeviceInfo& dev, 
   const int per_cu = dev.paged_wgs_per_cu > 0 ? dev.paged_wgs_per_cu : 1;
   const int64_t grid = (int64_t)(dev.cu_count > 0 ? dev.cu_count : 256) * per_cu;
   const bool vec = (a.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0;
-  // pages the block tables can name: every unit's rows clamped to the table and the width
-  const int64_t table_pages = std::min<int64_t>(a.max_pages, ((int64_t)a.width + kPage - 1) / kPage);
-  const bool large = (int64_t)a.B * qgroups * table_pages >= kChunkLargeMinPages;
+  // the fragment maxima leave as 16-byte stores from the staged chunk: aligned rows only
+  if (a.frag_max != nullptr &&
+      (!vec || (reinterpret_cast<uintptr_t>(a.frag_max) & 15) != 0 || a.frag.fpc != 4 * chunk_pages(a, qgroups)))
+    return hipErrorInvalidValue;
+  const bool large = chunk_pages(a, qgroups) == kChunkLarge;
   const dim3 g((unsigned)grid), blk(64 * kPagedWaves);
   if (vec && large)
     hipLaunchKernelGGL((logits_paged_kernel<kPagedDepth, true, kChunkLarge>), g, blk, 0, s, a, qgroups);

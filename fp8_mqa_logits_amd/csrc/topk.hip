@@ -87,7 +87,8 @@ struct TopkKernelArgs {
   int32_t row0;
   TopkMap map;
   const uint32_t* frag_max;   // per (row, 16-key fragment) largest key code, or null
-  int64_t ld_frag;
+  FragLayout frag;            // its layout (launch.hpp)
+  int32_t frag_next_n;        // rows per request of the logits launch that wrote it
 };
 
 constexpr int kDigitBits = 11;
@@ -472,10 +473,18 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkKernelArgs a) {
   uint32_t fc[FM ? kSampleRuns : 1];
   if constexpr (FM) {
     if (a.frag_max != nullptr) {
+      // this row's unit and row slot in the chunk-major layout of the paged logits kernel
+      const int nn = a.frag_next_n;
+      const int rb = row / nn, rt = row - rb * nn;
+      const int64_t base = ((int64_t)rb * ((nn + 3) / 4) + rt / 4) * a.frag.unit_stride + (rt & 3) * a.frag.fpc;
+      const int64_t blk = (int64_t)a.frag.rows * a.frag.fpc;
+      const int64_t per_row = a.frag.unit_stride / a.frag.rows;   // fragments of a row in the layout
 #pragma unroll
       for (int b = 0; b < kSampleRuns; ++b) {
         const int f = b * THREADS + tid;
-        fc[b] = f < a.ld_frag ? a.frag_max[(int64_t)row * a.ld_frag + f] : 0u;
+        const int c = f / a.frag.fpc;
+        const int64_t idx = base + c * blk + (f - c * a.frag.fpc);
+        fc[b] = f < per_row && idx < a.frag.elems ? a.frag_max[idx] : 0u;
       }
     }
   }
@@ -1149,7 +1158,8 @@ hipError_t launch_topk(const TopkArgs& ta, const TopkPlan& plan, void* ws, hipSt
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     if (L.cfg == 2 && ta.frag_max != nullptr && vec4 && ta.ks == nullptr) {
       a.frag_max = ta.frag_max;
-      a.ld_frag = ta.ld_frag;
+      a.frag = ta.frag;
+      a.frag_next_n = ta.frag_next_n;
       launch_wide_frag_max((unsigned)grid, a, s);
     } else if (L.cfg == 2) {
       launch_vec<kWideThreads, kSmallCap, (int)kWideSeg, true, true>(vec4, (unsigned)grid, a, s);
