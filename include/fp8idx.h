@@ -270,7 +270,9 @@ FP8IDX_API fp8idx_status indexer_logits_topk_ragged_overlap(const uint8_t* q, co
  * request's next_n rows exceed the cap.  When a chunk's top-k takes one
  * workgroup per row (at most 512 rows of at most 131072 keys, k up to about
  * 2300), the logits kernel also writes each row's largest logit per 16-key
- * fragment into the workspace (ceil(width / 16) words per row), and the top-k
+ * fragment into the workspace (one word per fragment of the width, rounded up
+ * to whole 1024-key blocks, per row slot: min(4, next_n) slots per group of 4
+ * rows; fp8idx_workspace_bytes_paged includes them), and the top-k
  * takes its threshold from those maxima: the kk-th largest of them is at most
  * the row's kk-th largest logit, and only fragments that reach it are read.
  * The result is the same exact selection either way.
