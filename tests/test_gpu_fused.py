@@ -116,6 +116,34 @@ def test_fused_paged_fragment_maxima(mode, k):
         assert set(got[i].tolist()) == set(want[i].tolist()), f"{mode} k{k} slots row {i}"
 
 
+@pytest.mark.parametrize("B,next_n,cap_requests", [(64, 1, 0), (20, 2, 8), (9, 6, 4)])
+def test_fused_paged_fragment_maxima_row_slots(B, next_n, cap_requests):
+    """The fragment maxima's chunk-major blocks with one row slot per block (next_n 1; 64 requests
+    over a 2048-page table take the 16-page chunks), two slots (next_n 2) and two 4-row groups per
+    request (next_n 6: a 4-row and a 2-row unit), over one or several workspace chunks.  Rows long
+    enough for the fragment-maxima path; checked against the exact selection on the device's logits."""
+    rng = np.random.default_rng(B * 10 + next_n)
+    ctx = rng.integers(50000, 131073, B)
+    ctx[0] = 131072
+    inp = paged_inputs(B, next_n, 0, 131072, 2048, seed=80 + next_n, ctx=ctx)
+    width = inp.max_pages * 64
+    args = [to_dev(a) for a in (inp.q, inp.kv_pool, inp.scale_pool, inp.weights, inp.row_len, inp.block_table)]
+    ld = (width + 3) // 4 * 4
+    cap = cap_requests * next_n * ld * 4
+    slots = F.indexer_logits_topk_paged(*args, inp.k, width=width, logits_cap_bytes=cap)
+    raw = F.indexer_logits_topk_paged(*args, inp.k, width=width, map_to_slots=False, logits_cap_bytes=cap)
+    logits = F.indexer_logits_paged(*args, width=width, clean=True)
+    torch.cuda.synchronize()
+    g = logits.cpu().numpy().astype(np.float64)
+    zeros = np.zeros(inp.rows, np.int64)
+    exact = topk_indices(g, zeros, inp.row_len, inp.k)
+    assert_topk_exact(raw.cpu().numpy(), exact, what=f"row slots B{B} next_n{next_n}")
+    want = map_block_table(exact, list(range(inp.rows)), next_n, inp.block_table, 64, inp.kv_pool.shape[0])
+    got = slots.cpu().numpy()
+    for i in range(inp.rows):
+        assert set(got[i].tolist()) == set(want[i].tolist()), f"B{B} next_n{next_n} slots row {i}"
+
+
 def _sample_rows(m, chunk):
     rows = {0, 1, m // 2, m - 2, m - 1}
     if chunk and chunk < m:
